@@ -1,0 +1,189 @@
+/*
+ * libmoe -- MoE layer forward on one AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument is a DEVICE pointer unless marked (host).
+ * The caller owns every buffer (inputs, outputs and the workspace); the
+ * library never allocates or frees memory, never synchronises the stream and
+ * keeps no state between calls. Every call validates its arguments on the
+ * host and then only enqueues kernels on `stream` (a hipStream_t passed as
+ * void*; NULL means the default stream); results are ready once the stream
+ * reaches that point. No C++ exception crosses this boundary.
+ *
+ * Layer (sources cited by page title and section):
+ *   y[t] = sum_{j < k, kept} w[t][j] * SwiGLU_{e(t,j)}(x[t]) + shared(x[t])
+ *   "FFN, SwiGLU and MoE" (bjdmk.com) sec. 3 (router r = W_r x, softmax,
+ *   top-k, weighted sum of the selected experts) and sec. 2 (SwiGLU);
+ *   "moe f&b compute flow" (Echo's blog): Router -> Dispatch -> FFN ->
+ *   Combine; "ops-transformer MoE operator on Ascend NPU" (gitcode.csdn.net):
+ *   the MoEForward sketch, capacity (pitfall 1), FP32 routing (pitfall 3);
+ *   "DeepSeek-V4.1-Flash fine-grained MoE (5A)" (openarchlab.com) sec. 1 and
+ *   3: selection by score + bias, raw sqrt(softplus) weights, SwiGLU clamp,
+ *   FP4 routed experts and one shared expert.
+ *
+ * Layouts (row-major, no padding):
+ *   x        [T][D]      act dtype (MOE_F32 or MOE_BF16)
+ *   W_r      [D][E]      fp32
+ *   bias     [E]         fp32
+ *   W_gate, W_up [E][D][F]  and  W_down [E][F][D]   w dtype F32 or BF16
+ *   MXFP4 weights keep the logical [E][K][N] matrix but are stored
+ *     K-contiguous per output column n: codes uint8 [E][N][K/2] (element
+ *     2i in the low nibble, 2i+1 in the high nibble), e8m0 scales uint8
+ *     [E][N][K/32] (scale 2^(s-127), s = 255 not allowed); for gate/up
+ *     K = D, N = F; for down K = F, N = D (OCP MX v1.0 e2m1 + e8m0).
+ *   Shared expert: Ws_gate, Ws_up [D][shared_F], Ws_down [shared_F][D], bf16.
+ *   topk_idx int32 [T][k], topk_w fp32 [T][k]   (slot 0 = largest key)
+ *   counts   int32 [E]      pairs routed to each expert, before capacity
+ *   offsets  int32 [E+1]    kept segment starts; offsets[E] = kept pairs A
+ *   slot_pos int32 [T][k]   row of (t, j) in the segments, -1 if dropped
+ *   perm_token int32 [T*k]  token of each segment row (rows < A written)
+ *   x_perm   [T*k][D] act dtype  H [T*k][F] act dtype  y_perm [T*k][D] fp32
+ *   y        [T][D]   act dtype
+ * Every device pointer must be 16-byte aligned.
+ *
+ * Errors: functions return MOE_OK (0) or a negative moe_status. Invalid
+ * arguments are rejected before anything is enqueued. MOE_ERR_HIP means a
+ * launch failed; moe_last_hip_error() then returns the hipError_t of the
+ * calling thread's last failure.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+typedef enum {
+  MOE_GATE_SOFTMAX = 0,       /* p = softmax(logit + bias) over all E */
+  MOE_GATE_SIGMOID = 1,       /* w = 1/(1+exp(-logit)) */
+  MOE_GATE_SQRT_SOFTPLUS = 2  /* w = sqrt(softplus(logit)) */
+} moe_gating;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or mode */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than needed */
+  MOE_ERR_HIP = -4           /* a HIP launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_WS_DISPATCH = 0,
+  MOE_WS_EXPERT_FFN = 1,
+  MOE_WS_FORWARD = 2
+} moe_ws_kind;
+
+/* Layer configuration (host struct, read during the call only).
+ *   T tokens (B*S flattened), D model width, E routed experts, F expert
+ *   width, top_k experts per token (1 <= top_k <= min(E, 16)).
+ *   gating    moe_gating.
+ *   renorm    1: divide the k selected weights by their sum (the module's
+ *             top-k renormalisation in "FFN, SwiGLU and MoE" sec. 3).
+ *   capacity  <= 0: unlimited; else each expert keeps at most `capacity`
+ *             pairs, the earliest tokens first ("ops-transformer" pitfall 1).
+ *   clamp     <= 0: none; else gate and up pre-activations are clamped to
+ *             [-clamp, clamp] before SiLU(gate)*up ("DeepSeek-V4.1-Flash"
+ *             sec. 1, 3), in routed and shared experts.
+ *   act_dtype MOE_F32 (then w_dtype MOE_F32) or MOE_BF16 (then w_dtype
+ *             MOE_BF16 or MOE_MXFP4).
+ *   shared_F  0: no shared expert; else the width of one always-on bf16
+ *             SwiGLU expert added with weight 1 (requires MOE_BF16). */
+typedef struct moe_cfg {
+  int32_t T, D, E, F, top_k;
+  int32_t gating;
+  int32_t renorm;
+  int32_t capacity;
+  float clamp;
+  int32_t act_dtype, w_dtype;
+  int32_t shared_F;
+} moe_cfg;
+
+/* Expert weights (host struct of device pointers). S_* are the e8m0 scale
+ * arrays for MXFP4 (NULL otherwise). Ws_* are the shared expert's (NULL
+ * when shared_F == 0). */
+typedef struct moe_weights {
+  const void *W_gate, *W_up, *W_down;
+  const uint8_t *S_gate, *S_up, *S_down;
+  const void *Ws_gate, *Ws_up, *Ws_down;
+} moe_weights;
+
+/* Bytes of workspace a call needs (host out-parameter `bytes`).
+ * MOE_WS_DISPATCH for moe_dispatch, MOE_WS_EXPERT_FFN for moe_expert_ffn,
+ * MOE_WS_FORWARD for moe_forward (holds x_perm, H, y_perm and, with a
+ * shared expert, its H and output). */
+int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes);
+
+/* Router ("FFN, SwiGLU and MoE" sec. 3; "ops-transformer" MoEForward steps
+ * 1-2, optimisation 2, pitfall 3; "DeepSeek-V4.1-Flash" sec. 1, 3;
+ * "MoE routing: Top-K, Expert-Choice and Sigmoid Gating").
+ *   logit[t][e] = fp32 fused multiply-add chain over d = 0..D-1 of
+ *                 x[t][d]*W_r[d][e], starting from +0 (bit-reproducible);
+ *   key = logit + bias[e] (bias may be NULL = 0); the k largest keys in
+ *   descending order, equal keys to the lower expert index, go to topk_idx;
+ *   topk_w by the gating mode (softmax uses the keys, sigmoid and
+ *   sqrt-softplus the raw logits), renormalised when cfg->renorm.
+ *   logits [T][E] fp32 is an optional output (NULL: not written). */
+int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
+              int32_t* topk_idx, float* topk_w, float* logits, void* stream);
+
+/* Dispatch ("moe f&b compute flow" Dispatch; "ops-transformer" MoEForward
+ * step 3 GetTokensForExpert/Gather, pitfall 1). Groups the (t, j) pairs by
+ * expert, token order inside each expert; pairs whose rank within their
+ * expert reaches cfg->capacity are dropped. Writes counts, offsets,
+ * slot_pos, perm_token and copies each kept pair's x row to x_perm.
+ * Integer outputs are deterministic and bit-exact. */
+int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                 int32_t* offsets, int32_t* slot_pos, int32_t* perm_token, void* x_perm,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Routed experts ("FFN, SwiGLU and MoE" sec. 2; "ops-transformer"
+ * optimisation 3, one launch over all experts' irregular segments):
+ * for every kept row r of expert e's segment,
+ *   H[r] = SiLU(clampL(x_perm[r] W_gate[e])) * clampL(x_perm[r] W_up[e])
+ *          (rounded to the act dtype), y_perm[r] = H[r] W_down[e] (fp32).
+ * Rows r >= offsets[E] are not written. */
+int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                   const moe_weights* w, void* H, float* y_perm, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Shared expert ("DeepSeek-V4.1-Flash" sec. 1, 3): the same SwiGLU with
+ * the bf16 weights Ws_* on every token. H_shared [T][shared_F] bf16 is
+ * scratch owned by the caller; y_shared [T][D] fp32. */
+int moe_shared_expert(const moe_cfg* cfg, const void* x, const moe_weights* w, void* H_shared,
+                      float* y_shared, void* stream);
+
+/* Combine ("moe f&b compute flow" Combine; "ops-transformer" Scatter and
+ * WeightedSum; "FFN, SwiGLU and MoE" sec. 3):
+ *   y[t] = sum over j ascending with slot_pos[t][j] >= 0 of
+ *          topk_w[t][j] * y_perm[slot_pos[t][j]]  (+ y_shared[t] if not NULL),
+ * accumulated in fp32, stored in the act dtype (round to nearest even). */
+int moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const float* y_shared, void* y, void* stream);
+
+/* The whole layer: route, dispatch, routed experts, shared expert (when
+ * cfg->shared_F > 0) and combine, enqueued back to back with no host
+ * synchronisation. topk_idx, topk_w, counts and offsets are optional
+ * outputs (NULL: kept in the workspace). */
+int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
+                const moe_weights* w, void* y, int32_t* topk_idx, float* topk_w,
+                int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a moe_status value (host pointer, never NULL). */
+const char* moe_status_string(int status);
+
+/* hipError_t of the calling thread's last MOE_ERR_HIP (0 if none). */
+int moe_last_hip_error(void);
+
+/* MOE_ABI_VERSION of the library. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,311 @@
+// libmoe C ABI: argument validation, workspace carving and launch order.
+// The operations themselves are described where they are declared
+// (include/moe.h) and implemented in the kernels' files.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dev_ok(const void* p) { return p != nullptr && aligned16(p); }
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+size_t act_size(const moe_cfg& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
+
+int check_cfg(const moe_cfg* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->D < 8 || c->E < 1 || c->F < 8 || c->top_k < 1) return MOE_ERR_INVALID_ARG;
+  if (c->D % 8 || c->F % 8) return MOE_ERR_INVALID_ARG;
+  if (c->top_k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->gating < MOE_GATE_SOFTMAX || c->gating > MOE_GATE_SQRT_SOFTPLUS) return MOE_ERR_INVALID_ARG;
+  if (c->renorm != 0 && c->renorm != 1) return MOE_ERR_INVALID_ARG;
+  if (isnan(c->clamp) || isinf(c->clamp)) return MOE_ERR_INVALID_ARG;
+  if (c->shared_F < 0) return MOE_ERR_INVALID_ARG;
+  const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32;
+  const bool bf = c->act_dtype == MOE_BF16 && (c->w_dtype == MOE_BF16 || c->w_dtype == MOE_MXFP4);
+  if (!f32 && !bf) return MOE_ERR_INVALID_ARG;
+  if (c->E > kMaxE || c->top_k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  // row and element indices are int32 on the device side
+  if ((long long)c->T * c->top_k > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  if (bf) {
+    if (c->D % 32 || c->F % 32) return MOE_ERR_UNSUPPORTED;  // GEMM K steps of 32
+  } else {
+    if (c->D > 16384 || c->F > 16384) return MOE_ERR_UNSUPPORTED;
+  }
+  if (c->shared_F > 0) {
+    if (c->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (c->shared_F % 32) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int check_weights(const moe_cfg& c, const moe_weights* w) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (!dev_ok(w->W_gate) || !dev_ok(w->W_up) || !dev_ok(w->W_down)) return MOE_ERR_INVALID_ARG;
+  if (c.w_dtype == MOE_MXFP4) {
+    if (!w->S_gate || !w->S_up || !w->S_down) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int check_shared(const moe_cfg& c, const moe_weights* w) {
+  if (c.shared_F == 0) return MOE_OK;
+  if (!w || !dev_ok(w->Ws_gate) || !dev_ok(w->Ws_up) || !dev_ok(w->Ws_down))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MOE_ERR_HIP;
+}
+
+// Sequential carving of a caller-provided workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  void* take(size_t bytes) {
+    off = moe::align_up(off, kAlign);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+size_t dispatch_ws(const moe_cfg& c) {
+  return moe::align_up((size_t)c.E * moe::num_chunks(c) * 4, kAlign);
+}
+size_t ffn_ws(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
+
+struct ForwardWs {
+  int32_t *idx, *counts, *offsets, *slot_pos, *perm, *chunk_ws, *tilemap;
+  float *w, *y_perm, *y_shared;
+  void *x_perm, *H, *H_shared;
+  size_t bytes;
+};
+
+ForwardWs carve_forward(const moe_cfg& c, void* ws) {
+  Carver cv(ws);
+  ForwardWs f;
+  const size_t tk = (size_t)c.T * c.top_k;
+  f.idx = static_cast<int32_t*>(cv.take(tk * 4));
+  f.w = static_cast<float*>(cv.take(tk * 4));
+  f.counts = static_cast<int32_t*>(cv.take((size_t)c.E * 4));
+  f.offsets = static_cast<int32_t*>(cv.take(((size_t)c.E + 1) * 4));
+  f.slot_pos = static_cast<int32_t*>(cv.take(tk * 4));
+  f.perm = static_cast<int32_t*>(cv.take(tk * 4));
+  f.chunk_ws = static_cast<int32_t*>(cv.take(dispatch_ws(c)));
+  f.tilemap = static_cast<int32_t*>(cv.take(ffn_ws(c)));
+  f.x_perm = cv.take(tk * c.D * act_size(c));
+  f.H = cv.take(tk * c.F * act_size(c));
+  f.y_perm = static_cast<float*>(cv.take(tk * c.D * 4));
+  f.H_shared = c.shared_F > 0 ? cv.take((size_t)c.T * c.shared_F * 2) : nullptr;
+  f.y_shared = c.shared_F > 0 ? static_cast<float*>(cv.take((size_t)c.T * c.D * 4)) : nullptr;
+  f.bytes = moe::align_up(cv.off, kAlign);
+  return f;
+}
+
+hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                          const moe_weights& w, void* H, float* y_perm, int32_t* tilemap,
+                          hipStream_t s) {
+  if (c.act_dtype == MOE_F32)
+    return moe::launch_ffn_f32(c, static_cast<const float*>(x_perm), offsets,
+                               static_cast<const float*>(w.W_gate), static_cast<const float*>(w.W_up),
+                               static_cast<const float*>(w.W_down), static_cast<float*>(H), y_perm, s);
+  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, s);
+  if (e != hipSuccess) return e;
+  const bool mx = c.w_dtype == MOE_MXFP4;
+  moe::GemmProblem g{};
+  g.tilemap = tilemap;
+  g.offsets = offsets;
+  g.rows = c.T * c.top_k;
+  g.max_tiles = moe::max_mtiles(c);
+  g.E = c.E;
+  g.mxfp4 = mx;
+  g.clamp = c.clamp;
+  // gate + up with the SwiGLU epilogue
+  g.A = x_perm;
+  g.K = c.D;
+  g.N = c.F;
+  g.B0 = w.W_gate;
+  g.B1 = w.W_up;
+  g.S0 = w.S_gate;
+  g.S1 = w.S_up;
+  g.out = H;
+  e = moe::launch_gemm_swiglu(g, s);
+  if (e != hipSuccess) return e;
+  // down
+  g.A = H;
+  g.K = c.F;
+  g.N = c.D;
+  g.B0 = w.W_down;
+  g.B1 = nullptr;
+  g.S0 = w.S_down;
+  g.S1 = nullptr;
+  g.out = y_perm;
+  return moe::launch_gemm_down(g, s);
+}
+
+hipError_t run_shared(const moe_cfg& c, const void* x, const moe_weights& w, void* H_shared,
+                      float* y_shared, hipStream_t s) {
+  moe::GemmProblem g{};
+  g.tilemap = nullptr;
+  g.offsets = nullptr;
+  g.rows = c.T;
+  g.max_tiles = moe::ceil_div(c.T, moe::kBM);
+  g.E = 1;
+  g.mxfp4 = 0;
+  g.clamp = c.clamp;
+  g.A = x;
+  g.K = c.D;
+  g.N = c.shared_F;
+  g.B0 = w.Ws_gate;
+  g.B1 = w.Ws_up;
+  g.out = H_shared;
+  hipError_t e = moe::launch_gemm_swiglu(g, s);
+  if (e != hipSuccess) return e;
+  g.A = H_shared;
+  g.K = c.shared_F;
+  g.N = c.D;
+  g.B0 = w.Ws_down;
+  g.B1 = nullptr;
+  g.out = y_shared;
+  return moe::launch_gemm_down(g, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return MOE_ABI_VERSION; }
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  switch (kind) {
+    case MOE_WS_DISPATCH: *bytes = dispatch_ws(*cfg); return MOE_OK;
+    case MOE_WS_EXPERT_FFN: *bytes = cfg->act_dtype == MOE_F32 ? 0 : ffn_ws(*cfg); return MOE_OK;
+    case MOE_WS_FORWARD: *bytes = carve_forward(*cfg, nullptr).bytes; return MOE_OK;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+}
+
+int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
+              int32_t* topk_idx, float* topk_w, float* logits, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!dev_ok(x) || !dev_ok(W_r) || !dev_ok(topk_idx) || !dev_ok(topk_w) || !opt_ok(bias) ||
+      !opt_ok(logits))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(moe::launch_router(*cfg, x, W_r, bias, topk_idx, topk_w, logits,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                 int32_t* offsets, int32_t* slot_pos, int32_t* perm_token, void* x_perm,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!dev_ok(topk_idx) || !dev_ok(x) || !dev_ok(counts) || !dev_ok(offsets) ||
+      !dev_ok(slot_pos) || !dev_ok(perm_token) || !dev_ok(x_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < dispatch_ws(*cfg)) return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(moe::launch_dispatch(*cfg, topk_idx, x, counts, offsets, slot_pos, perm_token,
+                                         x_perm, static_cast<int32_t*>(ws),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                   const moe_weights* w, void* H, float* y_perm, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
+  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(H) || !dev_ok(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
+    return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(run_expert_ffn(*cfg, x_perm, offsets, *w, H, y_perm,
+                                   static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+int moe_shared_expert(const moe_cfg* cfg, const void* x, const moe_weights* w, void* H_shared,
+                      float* y_shared, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->shared_F == 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_shared(*cfg, w)) != MOE_OK) return st;
+  if (!dev_ok(x) || !dev_ok(H_shared) || !dev_ok(y_shared)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(run_shared(*cfg, x, *w, H_shared, y_shared, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const float* y_shared, void* y, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!dev_ok(y_perm) || !dev_ok(slot_pos) || !dev_ok(topk_w) || !opt_ok(y_shared) || !dev_ok(y))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(moe::launch_combine(*cfg, y_perm, slot_pos, topk_w, y_shared, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
+                const moe_weights* w, void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
+  if ((st = check_shared(*cfg, w)) != MOE_OK) return st;
+  if (!dev_ok(x) || !dev_ok(W_r) || !opt_ok(bias) || !dev_ok(y) || !opt_ok(topk_idx) ||
+      !opt_ok(topk_w) || !opt_ok(counts) || !opt_ok(offsets))
+    return MOE_ERR_INVALID_ARG;
+  const ForwardWs f0 = carve_forward(*cfg, nullptr);
+  if (!ws || !aligned16(ws) || ws_bytes < f0.bytes) return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  const moe_cfg& c = *cfg;
+  const ForwardWs f = carve_forward(c, ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : f.idx;
+  float* tw = topk_w ? topk_w : f.w;
+  int32_t* cnt = counts ? counts : f.counts;
+  int32_t* off = offsets ? offsets : f.offsets;
+  hipError_t e = moe::launch_router(c, x, W_r, bias, idx, tw, nullptr, s);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch(c, idx, x, cnt, off, f.slot_pos, f.perm, f.x_perm, f.chunk_ws, s);
+  if (e == hipSuccess) e = run_expert_ffn(c, f.x_perm, off, *w, f.H, f.y_perm, f.tilemap, s);
+  if (e == hipSuccess && c.shared_F > 0) e = run_shared(c, x, *w, f.H_shared, f.y_shared, s);
+  if (e == hipSuccess) e = moe::launch_combine(c, f.y_perm, f.slot_pos, tw, f.y_shared, y, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

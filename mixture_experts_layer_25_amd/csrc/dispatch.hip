@@ -1,0 +1,183 @@
+// Dispatch: group (token, slot) pairs by expert in token order, apply the
+// capacity, and copy each kept pair's x row into its expert's segment.
+//
+// "moe f&b compute flow" (Echo's blog), Dispatch: tokens go to the input
+// buffer of the experts the router picked. "ops-transformer MoE operator on
+// Ascend NPU": MoEForward step 3 gathers each expert's tokens; pitfall 1
+// caps each expert at `capacity` tokens and drops the overflow.
+//
+// The rank of pair (t, j) routed to e is the number of pairs before it in
+// (token, slot) order that are routed to e, so segments keep token order and
+// the drops are the latest tokens. Four launches, all integer work except
+// the row copy, all deterministic:
+//   count: per 256-token chunk, per-expert histogram (LDS integer atomics;
+//          counts do not depend on their order) -> chunk_ws[e][chunk];
+//   scan:  one wave per expert, exclusive scan over chunks -> the chunk's
+//          base rank, and the expert's total count;
+//   rank:  per chunk, kept counts -> offsets (every workgroup rescans the
+//          E counts; E <= 1024), then each pair's rank = chunk base + earlier
+//          waves' counts + earlier pairs in the wave (a broadcast scan over
+//          LDS) -> slot_pos, perm_token;
+//   copy:  one wave per token reads the row once (16-byte vectors) and
+//          writes it to each kept slot.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int T,
+                                                             int E, int k, int nchunks,
+                                                             int32_t* __restrict__ chunk_ws) {
+  __shared__ int hist[kMaxE];
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x;
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int t = chunk * kChunk + tid;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) chunk_ws[(size_t)e * nchunks + chunk] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int E, int nchunks,
+                                                            int32_t* __restrict__ chunk_ws,
+                                                            int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  int32_t* row = chunk_ws + (size_t)e * nchunks;
+  int running = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < nchunks ? row[c] : 0;
+    const int incl = wave_inclusive_scan(v);
+    if (c < nchunks) row[c] = running + incl - v;
+    running += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) counts[e] = running;
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ chunk_ws, int T, int E, int k, int capacity, int nchunks,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_pos, int32_t* __restrict__ perm) {
+  __shared__ int off_sh[kMaxE + 1];
+  __shared__ int wh[4][kMaxE];
+  __shared__ int idx_sh[256][kMaxK];
+  __shared__ int wave_tot[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int chunk = blockIdx.x;
+
+  // kept counts -> exclusive scan over experts (4 experts per thread)
+  int kept[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    int c = e < E ? counts[e] : 0;
+    if (capacity > 0 && c > capacity) c = capacity;
+    kept[q] = c;
+    local += c;
+  }
+  const int incl = wave_inclusive_scan(local);
+  if (lane == 63) wave_tot[wave] = incl;
+  for (int e = tid; e < E; e += 256) {
+    wh[0][e] = 0;
+    wh[1][e] = 0;
+    wh[2][e] = 0;
+    wh[3][e] = 0;
+  }
+  __syncthreads();
+  int base = incl - local;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < E) off_sh[e] = base;
+    base += kept[q];
+  }
+  if (tid == 255) off_sh[E] = base;  // total kept (thread 255 covers e >= E - 1)
+
+  // this chunk's pairs: LDS copy and per-wave histograms
+  const int t = chunk * kChunk + tid;
+  const bool valid_t = t < T;
+  for (int j = 0; j < k; ++j) {
+    const int e = valid_t ? idx[(size_t)t * k + j] : -1;
+    idx_sh[tid][j] = e;
+    if (e >= 0 && e < E) atomicAdd(&wh[wave][e], 1);
+  }
+  __syncthreads();
+  if (chunk == 0) {
+    for (int e = tid; e <= E; e += 256) offsets[e] = off_sh[e];
+  }
+  if (!valid_t) return;
+
+  for (int j = 0; j < k; ++j) {
+    const int e = idx_sh[tid][j];
+    int slot = -1;
+    if (e >= 0 && e < E) {
+      int r = chunk_ws[(size_t)e * nchunks + chunk];
+      for (int w = 0; w < wave; ++w) r += wh[w][e];
+      // earlier tokens of this wave
+      const int* wbase = &idx_sh[wave * 64][0];
+      for (int l = 0; l < lane; ++l)
+        for (int jj = 0; jj < k; ++jj) r += (wbase[l * kMaxK + jj] == e);
+      // earlier slots of this token
+      for (int jj = 0; jj < j; ++jj) r += (idx_sh[tid][jj] == e);
+      if (capacity <= 0 || r < capacity) {
+        slot = off_sh[e] + r;
+        perm[slot] = t;
+      }
+    }
+    slot_pos[(size_t)t * k + j] = slot;
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restrict__ x,
+                                                            const int32_t* __restrict__ slot_pos,
+                                                            int T, int k, int nvec,
+                                                            uint4* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int pos[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
+  const uint4* src = x + (size_t)t * nvec;
+  for (int v = lane; v < nvec; v += 64) {
+    const uint4 val = src[v];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (pos[j] >= 0) x_perm[(size_t)pos[j] * nvec + v] = val;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,
+                           int32_t* chunk_ws, hipStream_t s) {
+  const int nchunks = num_chunks(c);
+  dispatch_count_kernel<<<nchunks, 256, 0, s>>>(idx, c.T, c.E, c.top_k, nchunks, chunk_ws);
+  dispatch_scan_kernel<<<ceil_div(c.E, 4), 256, 0, s>>>(c.E, nchunks, chunk_ws, counts);
+  dispatch_rank_kernel<<<nchunks, 256, 0, s>>>(idx, counts, chunk_ws, c.T, c.E, c.top_k,
+                                               c.capacity, nchunks, offsets, slot_pos, perm);
+  const size_t row_bytes = (size_t)c.D * (c.act_dtype == MOE_BF16 ? 2 : 4);
+  dispatch_copy_kernel<<<ceil_div(c.T, 4), 256, 0, s>>>(
+      static_cast<const uint4*>(x), slot_pos, c.T, c.top_k, static_cast<int>(row_bytes / 16),
+      static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,68 @@
+// Internal launchers of libmoe (host side). Each enqueues kernels on the
+// given stream and returns hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Rows per M-tile of the grouped GEMMs (both projections).
+constexpr int kBM = 128;
+// Tokens per dispatch chunk (one workgroup of the count and rank kernels).
+constexpr int kChunk = 256;
+
+inline int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Upper bound of the number of M-tiles: every kept row in a full tile plus
+// one partial tile per expert.
+inline int max_mtiles(const moe_cfg& c) { return ceil_div((long long)c.T * c.top_k, kBM) + c.E; }
+// int32 entries of the tile map: [0] = tile count, then (expert, row0) pairs.
+inline size_t tilemap_ints(const moe_cfg& c) { return 1 + 2 * (size_t)max_mtiles(c); }
+inline int num_chunks(const moe_cfg& c) { return ceil_div(c.T, kChunk); }
+
+hipError_t launch_router(const moe_cfg& c, const void* x, const float* W_r, const float* bias,
+                         int32_t* idx, float* w, float* logits, hipStream_t s);
+
+// chunk_ws: int32 [E][num_chunks]
+hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,
+                           int32_t* chunk_ws, hipStream_t s);
+
+// Builds the tile map (tilemap_ints(c) int32) from device offsets.
+hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap, hipStream_t s);
+
+// bf16 activations: grouped MFMA GEMMs over the tile map. A dense launch
+// (tilemap == nullptr) treats rows [0, rows) as one segment of expert 0.
+struct GemmProblem {
+  const void* A;           // [rows][K] bf16
+  const int32_t* tilemap;  // nullptr: dense
+  const int32_t* offsets;  // segment ends (offsets[e+1]); unused when dense
+  int rows;                // dense row count / grid bound
+  int max_tiles;           // M-tiles in the grid
+  int K, N;
+  int E;
+  const void* B0;          // gate (SwiGLU) or down; [E][K][N] bf16 or MXFP4 codes [E][N][K/2]
+  const void* B1;          // up (SwiGLU), else nullptr
+  const uint8_t* S0;       // MXFP4 scales [E][N][K/32]
+  const uint8_t* S1;
+  int mxfp4;
+  float clamp;
+  void* out;               // SwiGLU: H bf16 [rows][N]; down: fp32 [rows][N]
+};
+hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);
+
+// fp32 activations and weights: straightforward VALU kernels.
+hipError_t launch_ffn_f32(const moe_cfg& c, const float* x_perm, const int32_t* offsets,
+                          const float* Wg, const float* Wu, const float* Wd, float* H,
+                          float* y_perm, hipStream_t s);
+
+hipError_t launch_combine(const moe_cfg& c, const float* y_perm, const int32_t* slot_pos,
+                          const float* topk_w, const float* y_shared, void* y, hipStream_t s);
+
+}  // namespace moe

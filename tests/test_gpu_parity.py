@@ -1,0 +1,113 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Integer results (indices, counts, offsets, slot positions, drops, perm) must
+be bit-exact, the router logits bit-identical (one fp32 fused multiply-add
+chain per logit on both sides), and y within 1e-4*max(1,|ref|) (fp32 layer)
+or 2e-2*max(1,|ref|) (bf16 / MXFP4 layers).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_25_amd import moe, synthetic as syn, upload
+from gpu_helpers import (act_to_f64, assert_close, check_routing, gpu_forward, sample_tokens,
+                         tol_for)
+
+pytestmark = pytest.mark.gpu
+
+# Small variants of the five workloads: same modes, sizes the oracle finishes
+# in seconds, several M- and N-tiles and ragged tails (F, D not multiples of
+# the 256/512-column tiles; T not a multiple of 128 rows).
+SMALL = {
+    "tiny_fp32": syn.CONFIGS["tiny_fp32"],
+    "mixtral": syn.small_variant(syn.CONFIGS["mixtral"], T=300, D=256, F=352),
+    "capacity": syn.small_variant(syn.CONFIGS["capacity"], T=500, D=256, F=256),
+    "fine128": syn.small_variant(syn.CONFIGS["fine128"], T=256, D=256, F=192),
+    "fine384_mxfp4": syn.small_variant(syn.CONFIGS["fine384_mxfp4"], T=200, D=256, F=128,
+                                       shared_F=96),
+}
+
+
+def _oracle_all(inp):
+    return oracle.forward(inp)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_stagewise(name):
+    cfg = SMALL[name]
+    print(f"[parity] small stagewise {name}: {cfg}", flush=True)
+    inp = syn.make_inputs(cfg)
+    ref = _oracle_all(inp)
+    got = gpu_forward(inp, stagewise=True)
+    check_routing(cfg, got, ref)
+    A = int(ref["offsets"][-1])
+    # x_perm rows are the byte-exact x rows of perm_token
+    assert np.array_equal(got["x_perm"][:A], inp.x[ref["perm"][:A]])
+    err = assert_close(got["y"], ref["y"], tol_for(cfg), f"{name} y")
+    print(f"[parity] {name}: max rel err {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_fused_equals_stagewise(name):
+    cfg = SMALL[name]
+    inp = syn.make_inputs(cfg)
+    a = gpu_forward(inp, stagewise=True)
+    b = gpu_forward(inp, stagewise=False)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(a["w"].view(np.uint32), b["w"].view(np.uint32))
+    assert np.array_equal(a["y"], b["y"]), "fused forward differs from the stage-by-stage calls"
+    c = gpu_forward(inp, stagewise=False)
+    assert np.array_equal(b["y"], c["y"]), "two runs differ (must be deterministic)"
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", syn.CONFIG_ORDER)
+def test_full_size(name):
+    """Full workload, in the launch configuration the benchmark times:
+    routing and dispatch on every token, y on sampled tokens."""
+    cfg = syn.CONFIGS[name]
+    print(f"[parity] full {name}: generating", flush=True)
+    inp = syn.make_inputs(cfg)
+    print(f"[parity] full {name}: gpu", flush=True)
+    got = gpu_forward(inp, stagewise=False)
+    print(f"[parity] full {name}: oracle routing", flush=True)
+    logits, idx, w = oracle.route(cfg, inp.x, inp.W_r, inp.bias)
+    counts, offsets, slot_pos, perm = oracle.dispatch(cfg, idx)
+    ref = dict(idx=idx, w=w, counts=counts, offsets=offsets)
+    check_routing(cfg, got, ref)
+    if cfg.capacity > 0:
+        assert (slot_pos < 0).any(), "capacity workload should drop pairs"
+    toks = sample_tokens(cfg, slot_pos, n=32 if cfg.T > 64 else cfg.T)
+    print(f"[parity] full {name}: oracle y on {len(toks)} tokens", flush=True)
+    y_exact, y_ref = oracle.forward_tokens(inp, idx, w, slot_pos, toks)
+    err = assert_close(got["y"][toks], y_ref, tol_for(cfg), f"{name} y")
+    print(f"[parity] full {name}: counts min {counts.min()} max {counts.max()} "
+          f"kept {offsets[-1]} of {cfg.T * cfg.k}; max rel err {err:.3g}", flush=True)
+
+
+def test_dense_gemm_path_vs_torch_matmul():
+    """The dense launch (one segment of all rows, used by the shared expert)
+    against torch matmuls in float32 on the CPU: H = SiLU(x Wg) * (x Wu)
+    rounded to bf16, y = H Wd."""
+    cfg = syn.Config("dense", T=333, D=512, E=1, k=1, F=64, shared_F=416, clamp=0.0)
+    inp = syn.make_inputs(cfg)
+    c, x, W_r, bias, w = upload.to_device(inp)
+    H, y = moe.shared_expert(c, x, w)
+    torch.cuda.synchronize()
+    xf = torch.from_numpy(syn.bf16_bits_to_f32(inp.x))
+    Wg = torch.from_numpy(syn.bf16_bits_to_f32(inp.Ws_gate))
+    Wu = torch.from_numpy(syn.bf16_bits_to_f32(inp.Ws_up))
+    Wd = torch.from_numpy(syn.bf16_bits_to_f32(inp.Ws_down))
+    g = xf @ Wg
+    u = xf @ Wu
+    h = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+    href = h.float().numpy()
+    hgot = H.float().cpu().numpy()
+    assert np.abs(hgot - href).max() <= 2 ** -7 * np.abs(href).max() + 1e-6
+    frac = np.mean(hgot != href)
+    assert frac < 2e-3, f"{frac:.2e} of H differ from the bf16-rounded torch value"
+    yref = (h.float() @ Wd).numpy()
+    ygot = y.cpu().numpy()
+    assert np.all(np.abs(ygot - yref) <= 2e-2 * np.maximum(1.0, np.abs(yref)))
+    assert np.abs(ygot - yref).max() < 1e-3 * np.abs(yref).max() + 1e-3
