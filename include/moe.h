@@ -152,6 +152,14 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offset
                    const moe_weights* w, void* H, float* y_perm, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* The two halves of moe_expert_ffn, for callers that schedule or time them
+ * separately. moe_expert_gate_up writes H only; moe_expert_down reads H and
+ * writes y_perm. Both take the same workspace as moe_expert_ffn. */
+int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                       const moe_weights* w, void* H, void* ws, size_t ws_bytes, void* stream);
+int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
+                    const moe_weights* w, float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* Shared expert ("DeepSeek-V4.1-Flash" sec. 1, 3): the same SwiGLU with
  * the bf16 weights Ws_* on every token. H_shared [T][shared_F] bf16 is
  * scratch owned by the caller; y_shared [T][D] fp32. */

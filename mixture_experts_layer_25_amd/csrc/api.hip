@@ -116,25 +116,28 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   return f;
 }
 
-hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
-                          const moe_weights& w, void* H, float* y_perm, int32_t* tilemap,
-                          hipStream_t s) {
-  if (c.act_dtype == MOE_F32)
-    return moe::launch_ffn_f32(c, static_cast<const float*>(x_perm), offsets,
-                               static_cast<const float*>(w.W_gate), static_cast<const float*>(w.W_up),
-                               static_cast<const float*>(w.W_down), static_cast<float*>(H), y_perm, s);
-  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, s);
-  if (e != hipSuccess) return e;
-  const bool mx = c.w_dtype == MOE_MXFP4;
+moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap) {
   moe::GemmProblem g{};
   g.tilemap = tilemap;
   g.offsets = offsets;
   g.rows = c.T * c.top_k;
   g.max_tiles = moe::max_mtiles(c);
   g.E = c.E;
-  g.mxfp4 = mx;
+  g.mxfp4 = c.w_dtype == MOE_MXFP4;
   g.clamp = c.clamp;
-  // gate + up with the SwiGLU epilogue
+  return g;
+}
+
+// gate + up with the SwiGLU epilogue -> H
+hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                       const moe_weights& w, void* H, int32_t* tilemap, hipStream_t s) {
+  if (c.act_dtype == MOE_F32)
+    return moe::launch_ffn_f32_gate_up(c, static_cast<const float*>(x_perm), offsets,
+                                       static_cast<const float*>(w.W_gate),
+                                       static_cast<const float*>(w.W_up), static_cast<float*>(H), s);
+  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, s);
+  if (e != hipSuccess) return e;
+  moe::GemmProblem g = routed_problem(c, offsets, tilemap);
   g.A = x_perm;
   g.K = c.D;
   g.N = c.F;
@@ -143,18 +146,36 @@ hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* o
   g.S0 = w.S_gate;
   g.S1 = w.S_up;
   g.out = H;
-  e = moe::launch_gemm_swiglu(g, s);
-  if (e != hipSuccess) return e;
-  // down
+  return moe::launch_gemm_swiglu(g, s);
+}
+
+// down projection -> y_perm; rebuild_map = false reuses the tile map that a
+// preceding run_gate_up left in the same workspace
+hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, const moe_weights& w,
+                    float* y_perm, int32_t* tilemap, bool rebuild_map, hipStream_t s) {
+  if (c.act_dtype == MOE_F32)
+    return moe::launch_ffn_f32_down(c, static_cast<const float*>(H), offsets,
+                                    static_cast<const float*>(w.W_down), y_perm, s);
+  if (rebuild_map) {
+    hipError_t e = moe::launch_tilemap(c, offsets, tilemap, s);
+    if (e != hipSuccess) return e;
+  }
+  moe::GemmProblem g = routed_problem(c, offsets, tilemap);
   g.A = H;
   g.K = c.F;
   g.N = c.D;
   g.B0 = w.W_down;
-  g.B1 = nullptr;
   g.S0 = w.S_down;
-  g.S1 = nullptr;
   g.out = y_perm;
   return moe::launch_gemm_down(g, s);
+}
+
+hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                          const moe_weights& w, void* H, float* y_perm, int32_t* tilemap,
+                          hipStream_t s) {
+  hipError_t e = run_gate_up(c, x_perm, offsets, w, H, tilemap, s);
+  if (e != hipSuccess) return e;
+  return run_down(c, H, offsets, w, y_perm, tilemap, false, s);
 }
 
 hipError_t run_shared(const moe_cfg& c, const void* x, const moe_weights& w, void* H_shared,
@@ -255,6 +276,32 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offset
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_expert_ffn(*cfg, x_perm, offsets, *w, H, y_perm,
                                    static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                       const moe_weights* w, void* H, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
+  if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(H)) return MOE_ERR_INVALID_ARG;
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
+    return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(run_gate_up(*cfg, x_perm, offsets, *w, H, static_cast<int32_t*>(ws),
+                                static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
+                    const moe_weights* w, float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
+  if (!dev_ok(H) || !dev_ok(offsets) || !dev_ok(y_perm)) return MOE_ERR_INVALID_ARG;
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
+    return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(run_down(*cfg, H, offsets, *w, y_perm, static_cast<int32_t*>(ws), true,
+                             static_cast<hipStream_t>(stream)));
 }
 
 int moe_shared_expert(const moe_cfg* cfg, const void* x, const moe_weights* w, void* H_shared,

@@ -103,13 +103,19 @@ hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* til
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_f32(const moe_cfg& c, const float* x_perm, const int32_t* offsets,
-                          const float* Wg, const float* Wu, const float* Wd, float* H,
-                          float* y_perm, hipStream_t s) {
+hipError_t launch_ffn_f32_gate_up(const moe_cfg& c, const float* x_perm, const int32_t* offsets,
+                                  const float* Wg, const float* Wu, float* H, hipStream_t s) {
   const int rows = c.T * c.top_k;
   if (rows == 0) return hipSuccess;
   ffn_f32_gateup_kernel<<<rows, 256, c.D * sizeof(float), s>>>(x_perm, offsets, c.E, c.D, c.F, Wg,
                                                                Wu, c.clamp, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_f32_down(const moe_cfg& c, const float* H, const int32_t* offsets,
+                               const float* Wd, float* y_perm, hipStream_t s) {
+  const int rows = c.T * c.top_k;
+  if (rows == 0) return hipSuccess;
   ffn_f32_down_kernel<<<rows, 256, c.F * sizeof(float), s>>>(H, offsets, c.E, c.D, c.F, Wd,
                                                              y_perm);
   return hipGetLastError();

@@ -17,18 +17,25 @@
 // (4 x 4 tiles, 256 fp32 accumulators per lane).
 //
 // Operands reach MFMA K-contiguous: a lane's fragment is 8 consecutive k of
-// one row (A) or one column (B). X rows are K-contiguous in memory. bf16
-// weights are [K][N] (N-contiguous), so each thread loads an 8 x 8 block
-// (8 rows of 16 bytes), transposes it in registers and writes 8 columns of
-// 8 k to LDS. MXFP4 weights are stored K-contiguous per column: a thread
-// loads one column's 32 codes and its scale and writes 32 exact bf16 values
-// (e2m1 times a power of two fits bf16 exactly).
+// one row (A) or one column (B).
+//   A (X rows, K-contiguous): 16-byte loads, stored as [row][4 k-groups] and
+//   read with ds_read_b128.
+//   B bf16 ([K][N], N-contiguous): whole 1 KB k-rows are stored untouched;
+//   the MFMA fragment is read with the gfx950 transposing LDS load
+//   ds_read_b64_tr_b16 (within a 16-lane group, lane i receives element i of
+//   the 4 rows the group points at), two per fragment, so no transpose runs
+//   on the vector ALUs.
+//   B MXFP4 (stored K-contiguous per column): each thread loads one column's
+//   32 codes and scale, converts them exactly to bf16 with
+//   v_cvt_scalef32_pk_bf16_fp4 and stores [column][4 k-groups] like A.
+// LDS 16-byte slots are XOR-swizzled (A and MXFP4 B: k-group ^ (row/2 mod 4);
+// bf16 B: chunk ^ 2*(k mod 4)) so that the lanes sharing an LDS cycle hit
+// distinct bank groups on the stores and on the MFMA fragment reads.
 //
-// LDS per stage: A [4 k-groups][128 rows] and B [4 k-groups][512 cols] of
-// 16-byte entries, rows/columns XOR-swizzled within groups of 8 so that the
-// 8 lanes sharing an LDS cycle hit 8 different 16-byte bank groups on both
-// the writes and the MFMA fragment reads. Two stages; the next stage's
-// global loads are in flight while the current stage's MFMAs run.
+// Pipeline: two LDS stages and two register sets. During step kt the MFMAs
+// read LDS stage kt, the registers holding step kt+1 are stored to the other
+// stage, and the global loads of step kt+2 are already in flight, so about
+// two steps of MFMA work cover the memory latency. One barrier per 32-k step.
 //
 // Workgroup -> tile: tiles are numbered M-tile fastest, so consecutive tiles
 // share one weight N-tile; workgroup b runs on XCD (b mod 8), and b is
@@ -63,8 +70,6 @@ struct Args {
   void* out;
 };
 
-__device__ __forceinline__ int swz_a(int m, int q) { return m ^ (((m >> 3) ^ (q << 1)) & 7); }
-__device__ __forceinline__ int swz_b(int n) { return n ^ ((n >> 3) & 7); }
 
 // e2m1 code -> binary32 bits (OCP MX v1.0: bit 3 sign, 2 exponent bits with
 // bias 1, 1 mantissa bit; exponent 0 encodes 0 and 0.5).
@@ -91,38 +96,46 @@ __device__ __forceinline__ float e8m0_scale(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-// Transpose an 8x8 bf16 block held as 8 rows (k) of 8 columns and write
-// column c (8 consecutive k) to its LDS entry.
-__device__ __forceinline__ void store_b_transposed(unsigned char* Bs, const uint4 (&rb)[8], int nb,
-                                                   int kb) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int p = c >> 1;
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x0 = u4get(rb[2 * q], p);
-      const uint32_t x1 = u4get(rb[2 * q + 1], p);
-      o[q] = (c & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
-    }
-    const int n = 8 * nb + c;
-    *reinterpret_cast<uint4*>(Bs + (kb * BNB + swz_b(n)) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+// Workgroup barrier for LDS hand-off: waits for this wave's LDS accesses,
+// not for its global loads in flight (a plain __syncthreads also drains
+// those, which would empty the prefetch pipeline).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// One column's 32 MXFP4 codes (k0..k0+31) and scale -> 4 LDS entries of
-// 8 bf16 each.
-__device__ __forceinline__ void store_b_mx(unsigned char* Bs, const uint4& codes, uint32_t s, int n) {
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// 32 MXFP4 codes of one column (k0..k0+31) and its scale -> 4 LDS entries of
+// 8 bf16 (k-group q at slot q ^ ((n >> 1) & 3) of the column's 64 bytes).
+// The hardware conversion scales each e2m1 pair by 2^(s-127) exactly; for
+// scale codes at the ends of the range the product is formed in fp32 instead.
+__device__ __forceinline__ void store_b_mx(unsigned char* Bs, u32x4_t codes, uint32_t s, int n) {
   const float sc = e8m0_scale(s);
+  const bool hw = s >= 2u && s <= 252u;
+  unsigned char* col = Bs + n * 64;
+  const int sw = (n >> 1) & 3;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t word = u4get(codes, q);  // codes of k = 8q .. 8q+7
-    uint4 o;
-    o.x = mx_pair(word & 0xFFu, sc);
-    o.y = mx_pair((word >> 8) & 0xFFu, sc);
-    o.z = mx_pair((word >> 16) & 0xFFu, sc);
-    o.w = mx_pair(word >> 24, sc);
-    *reinterpret_cast<uint4*>(Bs + (q * BNB + swz_b(n)) * 16) = o;
+    const uint32_t word = codes[q];  // codes of k = 8q .. 8q+7
+    u32x4_t o;
+    if (hw) {
+      o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
+      o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
+      o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
+      o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
+    } else {
+      o.x = mx_pair(word & 0xFFu, sc);
+      o.y = mx_pair((word >> 8) & 0xFFu, sc);
+      o.z = mx_pair((word >> 16) & 0xFFu, sc);
+      o.w = mx_pair(word >> 24, sc);
+    }
+    *reinterpret_cast<u32x4_t*>(col + ((q ^ sw) * 16)) = o;
   }
 }
 
@@ -154,39 +167,43 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
   }
   const int K = a.K, N = a.N;
   const int n0 = MODE == MODE_SWIGLU ? nt * 256 : nt * 512;
+  const int nk = K / BK;
 
-  // ---- global -> register staging
-  // A: 2 x 16 bytes per thread: rows tid/4 and tid/4 + 64, k-group tid%4
-  const int a_q = tid & 3;
-  const int a_m0 = tid >> 2, a_m1 = a_m0 + 64;
-  const uint16_t* a_src0 = a.A + (size_t)min(row0 + a_m0, row_end - 1) * K + 8 * a_q;
-  const uint16_t* a_src1 = a.A + (size_t)min(row0 + a_m1, row_end - 1) * K + 8 * a_q;
-  const int a_off0 = (a_q * BM + swz_a(a_m0, a_q)) * 16;
-  const int a_off1 = (a_q * BM + swz_a(a_m1, a_q)) * 16;
-  // B (bf16 [K][N]): an 8 x 8 block, columns 8*nb.., rows 8*kb..
-  const int nb = tid & 63, kb = tid >> 6;
-  const uint16_t* b_src = nullptr;
-  bool b_ok = false;
-  // B (MXFP4 [N][K/2]): LDS columns tid and tid + 256
-  const uint8_t* mx_src0 = nullptr;
-  const uint8_t* mx_src1 = nullptr;
-  const uint8_t* mx_scl0 = nullptr;
-  const uint8_t* mx_scl1 = nullptr;
-  bool mx_ok0 = false, mx_ok1 = false;
+  // ---- A: LDS [128 rows][4 slots of 8 k], 64 bytes per row; k-group q of
+  // row m sits at slot q ^ ((m >> 1) & 3). Thread t moves chunks t and
+  // t + 256 (row chunk/4, k-group chunk%4): 4 threads read 64 contiguous
+  // bytes of a row.
+  const int am0 = tid >> 2, am1 = am0 + 64, aq = tid & 3;
+  const uint16_t* a_g0 = a.A + (size_t)min(row0 + am0, row_end - 1) * K + 8 * aq;
+  const uint16_t* a_g1 = a.A + (size_t)min(row0 + am1, row_end - 1) * K + 8 * aq;
+  const int a_l0 = am0 * 64 + ((aq ^ ((am0 >> 1) & 3)) * 16);
+  const int a_l1 = am1 * 64 + ((aq ^ ((am1 >> 1) & 3)) * 16);
+
+  // ---- B bf16 ([K][N] rows): LDS [32 k-rows][64 chunks of 8 columns],
+  // 1 KB per row; chunk c of row k sits at slot c ^ (2*(k & 3)). Wave w
+  // moves rows 8w..8w+7, lane l chunk l of each: 512 contiguous bytes of
+  // W_gate and of W_up (or 1 KB of W_down) per row.
+  const uint16_t* b_g = nullptr;
   if (!MX) {
     int col;
     const uint16_t* base;
     if (MODE == MODE_SWIGLU) {
-      const bool up = nb >= 32;
-      col = n0 + 8 * (nb & 31);
-      base = static_cast<const uint16_t*>(up ? a.B1 : a.B0);
+      col = n0 + 8 * (lane & 31);
+      base = static_cast<const uint16_t*>(lane >= 32 ? a.B1 : a.B0);
     } else {
-      col = n0 + 8 * nb;
+      col = n0 + 8 * lane;
       base = static_cast<const uint16_t*>(a.B0);
     }
-    b_ok = col + 8 <= N;
-    b_src = base + ((size_t)e * K + 8 * kb) * N + (b_ok ? col : 0);
-  } else {
+    if (col + 8 > N) col = 0;  // columns past N: any valid data, never stored
+    b_g = base + ((size_t)e * K + 8 * wave) * N + col;
+  }
+  // ---- B MXFP4 (K-contiguous codes per column): LDS [512 columns][4 slots]
+  // like A; thread t converts columns t and t + 256.
+  const uint8_t* mx_src0 = nullptr;
+  const uint8_t* mx_src1 = nullptr;
+  const uint8_t* mx_scl0 = nullptr;
+  const uint8_t* mx_scl1 = nullptr;
+  if (MX) {
     int col0, col1;
     const uint8_t *codes0, *codes1, *scl0, *scl1;
     if (MODE == MODE_SWIGLU) {
@@ -201,50 +218,64 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
       codes0 = codes1 = static_cast<const uint8_t*>(a.B0);
       scl0 = scl1 = a.S0;
     }
-    mx_ok0 = col0 < N;
-    mx_ok1 = col1 < N;
-    const size_t r0 = (size_t)e * N + (mx_ok0 ? col0 : 0);
-    const size_t r1 = (size_t)e * N + (mx_ok1 ? col1 : 0);
+    const size_t r0 = (size_t)e * N + (col0 < N ? col0 : 0);
+    const size_t r1 = (size_t)e * N + (col1 < N ? col1 : 0);
     mx_src0 = codes0 + r0 * (K / 2);
     mx_src1 = codes1 + r1 * (K / 2);
     mx_scl0 = scl0 + r0 * (K / 32);
     mx_scl1 = scl1 + r1 * (K / 32);
   }
 
-  uint4 ra0, ra1;
-  uint4 rb[8];
-  uint4 rm0, rm1;
-  uint32_t rs0 = 127u, rs1 = 127u;
-
-#define MOE_LOAD_GLOBAL(k0)                                                                   \
-  do {                                                                                        \
-    ra0 = *reinterpret_cast<const uint4*>(a_src0 + (k0));                                    \
-    ra1 = *reinterpret_cast<const uint4*>(a_src1 + (k0));                                    \
-    if (!MX) {                                                                                \
-      _Pragma("unroll") for (int r = 0; r < 8; ++r) rb[r] =                                   \
-          b_ok ? *reinterpret_cast<const uint4*>(b_src + (size_t)((k0) + r) * N)              \
-               : make_uint4(0, 0, 0, 0);                                                      \
-    } else {                                                                                  \
-      rm0 = mx_ok0 ? *reinterpret_cast<const uint4*>(mx_src0 + (k0) / 2) : make_uint4(0, 0, 0, 0); \
-      rm1 = mx_ok1 ? *reinterpret_cast<const uint4*>(mx_src1 + (k0) / 2) : make_uint4(0, 0, 0, 0); \
-      rs0 = mx_ok0 ? mx_scl0[(k0) / 32] : 127u;                                               \
-      rs1 = mx_ok1 ? mx_scl1[(k0) / 32] : 127u;                                               \
-    }                                                                                         \
+  // One stage's worth of global data waits in registers between its load
+  // and its LDS store; there are two such register sets (suffix 0 / 1).
+#define MOE_DECL_SET(S)                                    \
+  u32x4_t ra0_##S, ra1_##S, rb_##S[8], rm0_##S, rm1_##S;  \
+  uint32_t rs0_##S = 127u, rs1_##S = 127u;
+#define MOE_LOAD_SET(S, kt_)                                                                   \
+  do {                                                                                         \
+    const int k0_ = (kt_) * BK;                                                                \
+    ra0_##S = *reinterpret_cast<const u32x4_t*>(a_g0 + k0_);                                     \
+    ra1_##S = *reinterpret_cast<const u32x4_t*>(a_g1 + k0_);                                     \
+    if (!MX) {                                                                                 \
+      const uint16_t* bp_ = b_g + (size_t)k0_ * N;                                             \
+      rb_##S[0] = *reinterpret_cast<const u32x4_t*>(bp_);                                        \
+      rb_##S[1] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)N);                            \
+      rb_##S[2] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)2 * N);                        \
+      rb_##S[3] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)3 * N);                        \
+      rb_##S[4] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)4 * N);                        \
+      rb_##S[5] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)5 * N);                        \
+      rb_##S[6] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)6 * N);                        \
+      rb_##S[7] = *reinterpret_cast<const u32x4_t*>(bp_ + (size_t)7 * N);                        \
+    } else {                                                                                   \
+      rm0_##S = *reinterpret_cast<const u32x4_t*>(mx_src0 + k0_ / 2);                            \
+      rm1_##S = *reinterpret_cast<const u32x4_t*>(mx_src1 + k0_ / 2);                            \
+      rs0_##S = mx_scl0[k0_ / 32];                                                             \
+      rs1_##S = mx_scl1[k0_ / 32];                                                             \
+    }                                                                                          \
   } while (0)
-
-#define MOE_STORE_LDS(stage)                                                                  \
-  do {                                                                                        \
-    unsigned char* As_ = smem + (stage) * STAGE;                                              \
-    unsigned char* Bs_ = As_ + A_STAGE;                                                       \
-    *reinterpret_cast<uint4*>(As_ + a_off0) = ra0;                                            \
-    *reinterpret_cast<uint4*>(As_ + a_off1) = ra1;                                            \
-    if (!MX) {                                                                                \
-      store_b_transposed(Bs_, rb, nb, kb);                                                    \
-    } else {                                                                                  \
-      store_b_mx(Bs_, rm0, rs0, tid);                                                         \
-      store_b_mx(Bs_, rm1, rs1, tid + 256);                                                   \
-    }                                                                                         \
+#define MOE_STORE_SET(S, stage_)                                                               \
+  do {                                                                                         \
+    unsigned char* As_ = smem + (stage_) * STAGE;                                              \
+    unsigned char* Bs_ = As_ + A_STAGE;                                                        \
+    *reinterpret_cast<u32x4_t*>(As_ + a_l0) = ra0_##S;                                           \
+    *reinterpret_cast<u32x4_t*>(As_ + a_l1) = ra1_##S;                                           \
+    if (!MX) {                                                                                 \
+      unsigned char* bw_ = Bs_ + (8 * wave) * 1024;                                            \
+      *reinterpret_cast<u32x4_t*>(bw_ + 0 * 1024 + ((lane ^ 0) * 16)) = rb_##S[0];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 1 * 1024 + ((lane ^ 2) * 16)) = rb_##S[1];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 2 * 1024 + ((lane ^ 4) * 16)) = rb_##S[2];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 3 * 1024 + ((lane ^ 6) * 16)) = rb_##S[3];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 4 * 1024 + ((lane ^ 0) * 16)) = rb_##S[4];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 5 * 1024 + ((lane ^ 2) * 16)) = rb_##S[5];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 6 * 1024 + ((lane ^ 4) * 16)) = rb_##S[6];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 7 * 1024 + ((lane ^ 6) * 16)) = rb_##S[7];               \
+    } else {                                                                                   \
+      store_b_mx(Bs_, rm0_##S, rs0_##S, tid);                                                  \
+      store_b_mx(Bs_, rm1_##S, rs1_##S, tid + 256);                                            \
+    }                                                                                          \
   } while (0)
+  MOE_DECL_SET(0)
+  MOE_DECL_SET(1)
 
   // wave's B-column bases in the tile
   int bcol[4];
@@ -264,15 +295,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = K / BK;
-  MOE_LOAD_GLOBAL(0);
-  MOE_STORE_LDS(0);
-  __syncthreads();
   const int lrow = lane & 31;
   const int lq = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) MOE_LOAD_GLOBAL((kt + 1) * BK);
+  // per-lane parts of the transposed B read (16-lane groups): k-row within
+  // 4, column offset
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  auto compute = [&](int stage) __attribute__((always_inline)) {
     const unsigned char* As = smem + stage * STAGE;
     const unsigned char* Bs = As + A_STAGE;
 #pragma unroll
@@ -280,20 +310,70 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
       const int q = 2 * kk + lq;
       bf16x8_t af[4], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (q * BM + swz_a(32 * i + lrow, q)) * 16);
+      for (int i = 0; i < 4; ++i) {
+        const int m = 32 * i + lrow;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + m * 64 + ((q ^ ((m >> 1) & 3)) * 16));
+      }
+      if (MX) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (q * BNB + swz_b(bcol[j] + lrow)) * 16);
+        for (int j = 0; j < 4; ++j) {
+          const int n = bcol[j] + lrow;
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + n * 64 + ((q ^ ((n >> 1) & 3)) * 16));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = bcol[j] + tr_col;
+          const int chunk = col >> 3;
+          const int byte = (col & 7) * 2;
+          const int r0 = 16 * kk + 8 * lq + tr_row;  // r0 & 3 == tr_row
+          const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(Bs + r0 * 1024 + ((chunk ^ (2 * tr_row)) * 16) + byte));
+          const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(Bs + (r0 + 4) * 1024 + ((chunk ^ (2 * tr_row)) * 16) + byte));
+          const s16x8_t hv = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          bfr[j] = __builtin_bit_cast(bf16x8_t, hv);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) MOE_STORE_LDS(stage ^ 1);
-    __syncthreads();
+  };
+
+  // Two register sets: while stage kt is multiplied from LDS, the data of
+  // stage kt+1 waits in one set to be stored and the loads of stage kt+2
+  // fill the other.
+  // While stage kt is multiplied from LDS, the registers holding step kt+1
+  // are stored to the other stage and the loads of step kt+2 fill the
+  // other register set.
+  // Loads are issued unconditionally (the last step's are repeated at the
+  // tail) so that the wait before each store covers only its own set.
+  MOE_LOAD_SET(0, 0);
+  MOE_LOAD_SET(1, min(1, nk - 1));
+  MOE_STORE_SET(0, 0);
+  block_barrier();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    MOE_LOAD_SET(0, min(kt + 2, nk - 1));
+    asm volatile("" ::: "memory");  // issue the loads before this step's LDS reads
+    compute(0);
+    asm volatile("" ::: "memory");  // keep the stores after this step's LDS reads
+    MOE_STORE_SET(1, 1);
+    block_barrier();
+    MOE_LOAD_SET(1, min(kt + 3, nk - 1));
+    asm volatile("" ::: "memory");
+    compute(1);
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) MOE_STORE_SET(0, 0);
+    block_barrier();
   }
+  if (kt < nk) compute(0);  // odd number of steps
+#undef MOE_DECL_SET
+#undef MOE_LOAD_SET
+#undef MOE_STORE_SET
 
   // ---- epilogue. Accumulator r of lane l: row 8*(r/4) + 4*(l/32) + r%4,
   // column l%32 of its 32x32 tile.
@@ -339,9 +419,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
     }
   }
 }
-
-#undef MOE_LOAD_GLOBAL
-#undef MOE_STORE_LDS
 
 hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;

@@ -58,9 +58,10 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);
 
 // fp32 activations and weights: straightforward VALU kernels.
-hipError_t launch_ffn_f32(const moe_cfg& c, const float* x_perm, const int32_t* offsets,
-                          const float* Wg, const float* Wu, const float* Wd, float* H,
-                          float* y_perm, hipStream_t s);
+hipError_t launch_ffn_f32_gate_up(const moe_cfg& c, const float* x_perm, const int32_t* offsets,
+                                  const float* Wg, const float* Wu, float* H, hipStream_t s);
+hipError_t launch_ffn_f32_down(const moe_cfg& c, const float* H, const int32_t* offsets,
+                               const float* Wd, float* y_perm, hipStream_t s);
 
 hipError_t launch_combine(const moe_cfg& c, const float* y_perm, const int32_t* slot_pos,
                           const float* topk_w, const float* y_shared, void* y, hipStream_t s);

@@ -50,6 +50,7 @@ class _Weights(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
+           "moe_expert_gate_up", "moe_expert_down",
            "moe_shared_expert", "moe_combine", "moe_forward", "moe_status_string",
            "moe_last_hip_error", "moe_version"]
 
@@ -69,6 +70,8 @@ def lib():
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [P, vp, vp, W, vp, vp, vp, sz, vp]
+    L.moe_expert_gate_up.argtypes = [P, vp, vp, W, vp, vp, sz, vp]
+    L.moe_expert_down.argtypes = [P, vp, vp, W, vp, vp, sz, vp]
     L.moe_shared_expert.argtypes = [P, vp, W, vp, vp, vp]
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.moe_forward.argtypes = [P, vp, vp, vp, W, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -77,7 +80,8 @@ def lib():
     L.moe_last_hip_error.restype = ctypes.c_int
     L.moe_version.restype = ctypes.c_int
     for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
-                 "moe_shared_expert", "moe_combine", "moe_forward"):
+                 "moe_expert_gate_up", "moe_expert_down", "moe_shared_expert", "moe_combine",
+                 "moe_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -189,6 +193,20 @@ def expert_ffn(cfg: Cfg, x_perm, offsets, weights: Weights, H=None, y_perm=None,
     _check(lib().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(offsets), ctypes.byref(w),
                                 _p(H), _p(y_perm), _p(ws), ws.numel(), _stream(stream)))
     return H, y_perm
+
+
+def expert_gate_up(cfg: Cfg, x_perm, offsets, weights: Weights, H, ws, stream=None, wstruct=None):
+    w = wstruct if wstruct is not None else weights.struct()
+    _check(lib().moe_expert_gate_up(ctypes.byref(cfg), _p(x_perm), _p(offsets), ctypes.byref(w),
+                                    _p(H), _p(ws), ws.numel(), _stream(stream)))
+    return H
+
+
+def expert_down(cfg: Cfg, H, offsets, weights: Weights, y_perm, ws, stream=None, wstruct=None):
+    w = wstruct if wstruct is not None else weights.struct()
+    _check(lib().moe_expert_down(ctypes.byref(cfg), _p(H), _p(offsets), ctypes.byref(w),
+                                 _p(y_perm), _p(ws), ws.numel(), _stream(stream)))
+    return y_perm
 
 
 def shared_expert(cfg: Cfg, x, weights: Weights, H_shared=None, y_shared=None, stream=None):
