@@ -29,13 +29,15 @@
 //   32 codes and scale, converts them exactly to bf16 with
 //   v_cvt_scalef32_pk_bf16_fp4 and stores [column][4 k-groups] like A.
 // LDS 16-byte slots are XOR-swizzled (A and MXFP4 B: k-group ^ (row/2 mod 4);
-// bf16 B: chunk ^ 2*(k mod 4)) so that the lanes sharing an LDS cycle hit
-// distinct bank groups on the stores and on the MFMA fragment reads.
+// bf16 B: chunk ^ 4*(k mod 4)) so that the 16 lanes sharing a 256-byte
+// LDS cycle (64 banks on gfx950) hit 16 distinct 16-byte bank groups on the
+// stores and on the MFMA fragment reads (checked with the LDS bank-conflict
+// counter).
 //
-// Pipeline: two LDS stages and two register sets. During step kt the MFMAs
-// read LDS stage kt, the registers holding step kt+1 are stored to the other
-// stage, and the global loads of step kt+2 are already in flight, so about
-// two steps of MFMA work cover the memory latency. One barrier per 32-k step.
+// Pipeline: two LDS stages and three register sets. During step kt the MFMAs
+// read LDS stage kt%2, the registers holding step kt+1 are stored to the
+// other stage, and the global loads of steps kt+2 and kt+3 are in flight.
+// One barrier per 32-k step.
 //
 // Workgroup -> tile: tiles are numbered M-tile fastest, so consecutive tiles
 // share one weight N-tile; workgroup b runs on XCD (b mod 8), and b is
@@ -88,6 +90,11 @@ __device__ __forceinline__ uint32_t mx_pair(uint32_t byte, float scale) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
+// Slot permutation of the 4 k-groups of a 64-byte row: rows r..r+15 then
+// put any one k-group in 16 distinct 16-byte bank groups, and so do rows
+// r..r+3 with all 4 k-groups (the store pattern).
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -112,14 +119,14 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 // 32 MXFP4 codes of one column (k0..k0+31) and its scale -> 4 LDS entries of
-// 8 bf16 (k-group q at slot q ^ ((n >> 1) & 3) of the column's 64 bytes).
+// 8 bf16 (k-group q at slot q ^ swz4(n) of the column's 64 bytes).
 // The hardware conversion scales each e2m1 pair by 2^(s-127) exactly; for
 // scale codes at the ends of the range the product is formed in fp32 instead.
 __device__ __forceinline__ void store_b_mx(unsigned char* Bs, u32x4_t codes, uint32_t s, int n) {
   const float sc = e8m0_scale(s);
   const bool hw = s >= 2u && s <= 252u;
   unsigned char* col = Bs + n * 64;
-  const int sw = (n >> 1) & 3;
+  const int sw = swz4(n);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t word = codes[q];  // codes of k = 8q .. 8q+7
@@ -170,14 +177,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
   const int nk = K / BK;
 
   // ---- A: LDS [128 rows][4 slots of 8 k], 64 bytes per row; k-group q of
-  // row m sits at slot q ^ ((m >> 1) & 3). Thread t moves chunks t and
+  // row m sits at slot q ^ swz4(m). Thread t moves chunks t and
   // t + 256 (row chunk/4, k-group chunk%4): 4 threads read 64 contiguous
   // bytes of a row.
   const int am0 = tid >> 2, am1 = am0 + 64, aq = tid & 3;
   const uint16_t* a_g0 = a.A + (size_t)min(row0 + am0, row_end - 1) * K + 8 * aq;
   const uint16_t* a_g1 = a.A + (size_t)min(row0 + am1, row_end - 1) * K + 8 * aq;
-  const int a_l0 = am0 * 64 + ((aq ^ ((am0 >> 1) & 3)) * 16);
-  const int a_l1 = am1 * 64 + ((aq ^ ((am1 >> 1) & 3)) * 16);
+  const int a_l0 = am0 * 64 + ((aq ^ swz4(am0)) * 16);
+  const int a_l1 = am1 * 64 + ((aq ^ swz4(am1)) * 16);
 
   // ---- B bf16 ([K][N] rows): LDS [32 k-rows][64 chunks of 8 columns],
   // 1 KB per row; chunk c of row k sits at slot c ^ (2*(k & 3)). Wave w
@@ -262,13 +269,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
     if (!MX) {                                                                                 \
       unsigned char* bw_ = Bs_ + (8 * wave) * 1024;                                            \
       *reinterpret_cast<u32x4_t*>(bw_ + 0 * 1024 + ((lane ^ 0) * 16)) = rb_##S[0];               \
-      *reinterpret_cast<u32x4_t*>(bw_ + 1 * 1024 + ((lane ^ 2) * 16)) = rb_##S[1];               \
-      *reinterpret_cast<u32x4_t*>(bw_ + 2 * 1024 + ((lane ^ 4) * 16)) = rb_##S[2];               \
-      *reinterpret_cast<u32x4_t*>(bw_ + 3 * 1024 + ((lane ^ 6) * 16)) = rb_##S[3];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 1 * 1024 + ((lane ^ 4) * 16)) = rb_##S[1];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 2 * 1024 + ((lane ^ 8) * 16)) = rb_##S[2];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 3 * 1024 + ((lane ^ 12) * 16)) = rb_##S[3];               \
       *reinterpret_cast<u32x4_t*>(bw_ + 4 * 1024 + ((lane ^ 0) * 16)) = rb_##S[4];               \
-      *reinterpret_cast<u32x4_t*>(bw_ + 5 * 1024 + ((lane ^ 2) * 16)) = rb_##S[5];               \
-      *reinterpret_cast<u32x4_t*>(bw_ + 6 * 1024 + ((lane ^ 4) * 16)) = rb_##S[6];               \
-      *reinterpret_cast<u32x4_t*>(bw_ + 7 * 1024 + ((lane ^ 6) * 16)) = rb_##S[7];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 5 * 1024 + ((lane ^ 4) * 16)) = rb_##S[5];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 6 * 1024 + ((lane ^ 8) * 16)) = rb_##S[6];               \
+      *reinterpret_cast<u32x4_t*>(bw_ + 7 * 1024 + ((lane ^ 12) * 16)) = rb_##S[7];               \
     } else {                                                                                   \
       store_b_mx(Bs_, rm0_##S, rs0_##S, tid);                                                  \
       store_b_mx(Bs_, rm1_##S, rs1_##S, tid + 256);                                            \
@@ -276,6 +283,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
   } while (0)
   MOE_DECL_SET(0)
   MOE_DECL_SET(1)
+  MOE_DECL_SET(2)
 
   // wave's B-column bases in the tile
   int bcol[4];
@@ -312,13 +320,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 32 * i + lrow;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + m * 64 + ((q ^ ((m >> 1) & 3)) * 16));
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + m * 64 + ((q ^ swz4(m)) * 16));
       }
       if (MX) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = bcol[j] + lrow;
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + n * 64 + ((q ^ ((n >> 1) & 3)) * 16));
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + n * 64 + ((q ^ swz4(n)) * 16));
         }
       } else {
 #pragma unroll
@@ -328,9 +336,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
           const int byte = (col & 7) * 2;
           const int r0 = 16 * kk + 8 * lq + tr_row;  // r0 & 3 == tr_row
           const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(Bs + r0 * 1024 + ((chunk ^ (2 * tr_row)) * 16) + byte));
+              (lds_s16x4_t*)(Bs + r0 * 1024 + ((chunk ^ (4 * tr_row)) * 16) + byte));
           const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(Bs + (r0 + 4) * 1024 + ((chunk ^ (2 * tr_row)) * 16) + byte));
+              (lds_s16x4_t*)(Bs + (r0 + 4) * 1024 + ((chunk ^ (4 * tr_row)) * 16) + byte));
           const s16x8_t hv = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
           bfr[j] = __builtin_bit_cast(bf16x8_t, hv);
         }
@@ -343,34 +351,45 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
     }
   };
 
-  // Two register sets: while stage kt is multiplied from LDS, the data of
-  // stage kt+1 waits in one set to be stored and the loads of stage kt+2
-  // fill the other.
-  // While stage kt is multiplied from LDS, the registers holding step kt+1
-  // are stored to the other stage and the loads of step kt+2 fill the
-  // other register set.
-  // Loads are issued unconditionally (the last step's are repeated at the
-  // tail) so that the wait before each store covers only its own set.
+  // Three register sets: while step kt is multiplied from LDS stage kt%2,
+  // the registers holding step kt+1 are stored to the other stage and the
+  // loads of steps kt+2 and kt+3 are in flight, so about three steps of
+  // MFMA work cover the memory latency. Loads are issued unconditionally
+  // (clamped to the last step) so that the wait before each store covers
+  // only its own set.
   MOE_LOAD_SET(0, 0);
   MOE_LOAD_SET(1, min(1, nk - 1));
+  MOE_LOAD_SET(2, min(2, nk - 1));
   MOE_STORE_SET(0, 0);
   block_barrier();
+#define MOE_STEP(L, S, k_)                                                  \
+  do {                                                                      \
+    MOE_LOAD_SET(L, min((k_) + 3, nk - 1));                                 \
+    asm volatile("" ::: "memory"); /* loads before this step's LDS reads */ \
+    compute((k_) & 1);                                                      \
+    asm volatile("" ::: "memory"); /* stores after this step's LDS reads */ \
+    MOE_STORE_SET(S, ((k_) + 1) & 1);                                       \
+    block_barrier();                                                        \
+  } while (0)
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    MOE_LOAD_SET(0, min(kt + 2, nk - 1));
-    asm volatile("" ::: "memory");  // issue the loads before this step's LDS reads
-    compute(0);
-    asm volatile("" ::: "memory");  // keep the stores after this step's LDS reads
-    MOE_STORE_SET(1, 1);
-    block_barrier();
-    MOE_LOAD_SET(1, min(kt + 3, nk - 1));
-    asm volatile("" ::: "memory");
-    compute(1);
-    asm volatile("" ::: "memory");
-    if (kt + 2 < nk) MOE_STORE_SET(0, 0);
-    block_barrier();
+  for (; kt + 3 < nk; kt += 3) {
+    MOE_STEP(0, 1, kt);
+    MOE_STEP(1, 2, kt + 1);
+    MOE_STEP(2, 0, kt + 2);
   }
-  if (kt < nk) compute(0);  // odd number of steps
+  // last 1..3 steps: their data is already in sets 0, 1, 2
+  compute(kt & 1);
+  if (kt + 1 < nk) {
+    MOE_STORE_SET(1, (kt + 1) & 1);
+    block_barrier();
+    compute((kt + 1) & 1);
+    if (kt + 2 < nk) {
+      MOE_STORE_SET(2, (kt + 2) & 1);
+      block_barrier();
+      compute((kt + 2) & 1);
+    }
+  }
+#undef MOE_STEP
 #undef MOE_DECL_SET
 #undef MOE_LOAD_SET
 #undef MOE_STORE_SET

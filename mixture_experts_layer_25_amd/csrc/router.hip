@@ -11,10 +11,12 @@
 // Each logit is one fp32 fused multiply-add chain over d = 0..D-1 from +0,
 // so every logit is bit-reproducible. The chain order rules out MFMA (whose
 // internal summation order is not specified); the work runs on the vector
-// ALUs: a workgroup stages a D-chunk of x (transposed, fp32) and of W_r in
-// LDS, and each thread keeps RT tokens x RE experts of accumulators in
-// registers. A token's experts live in NE adjacent lanes, so top-k is a
-// butterfly arg-max over those lanes, k times, with no sorting.
+// ALUs: a workgroup stages D-chunks of x (transposed, fp32) and of W_r in a
+// double-buffered LDS area (the next chunk's loads fly while the current one
+// is multiplied), and each thread keeps RT tokens x RE experts of
+// accumulators in registers. A token's experts live in NE adjacent lanes,
+// so top-k is a butterfly arg-max over those lanes, k times, with no
+// sorting.
 #include <math.h>
 
 #include "common.h"
@@ -40,13 +42,18 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   constexpr int NT = 256 / NE;  // token groups per workgroup
   constexpr int TB = NT * RT;   // tokens per workgroup
   constexpr int EP = NE * RE;   // experts, padded
-  __shared__ float xs[DK][TB];
-  __shared__ float wsm[DK][EP];
+  constexpr int VX = XBF16 ? 8 : 4;                     // x values per 16-byte load
+  constexpr int NXV = (TB * DK / VX + 255) / 256;      // x loads per thread per chunk
+  constexpr int NWV = (DK * EP / 4 + 255) / 256;       // W_r loads per thread per chunk
+  __shared__ float xs[2][DK][TB];
+  __shared__ float wsm[2][DK][EP];
 
   const int tid = threadIdx.x;
   const int te = tid % NE;
   const int tt = tid / NE;
   const int t0 = blockIdx.x * TB;
+  const int D = a.D, E = a.E;
+  const bool wvec = (E & 3) == 0;
 
   float acc[RT][RE];
 #pragma unroll
@@ -54,50 +61,117 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
     for (int j = 0; j < RE; ++j) acc[i][j] = 0.0f;
 
-  for (int d0 = 0; d0 < a.D; d0 += DK) {
-    const int dk = min(DK, a.D - d0);
-    __syncthreads();
-    for (int q = tid; q < TB * DK; q += 256) {
-      const int tl = q / DK, dd = q % DK;
-      const int t = t0 + tl;
-      float v = 0.0f;
-      if (t < a.T && dd < dk) {
-        const size_t off = (size_t)t * a.D + d0 + dd;
-        v = XBF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[off])
-                  : static_cast<const float*>(a.x)[off];
+  // Chunk c covers d = c*DK .. c*DK+DK-1. Its x rows (TB tokens) and W_r
+  // rows go global -> registers -> LDS (x transposed to [d][token], fp32);
+  // the next chunk's loads are in flight while this one is multiplied.
+  uint4 rx[NXV];
+  float4 rw[NWV];
+  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    const int d0 = c * DK;
+#pragma unroll
+    for (int i = 0; i < NXV; ++i) {
+      const int v = tid + 256 * i;
+      const int tl = v / (DK / VX), dg = v % (DK / VX);
+      const int t = t0 + tl, d = d0 + VX * dg;
+      rx[i] = make_uint4(0, 0, 0, 0);
+      if (v < TB * DK / VX && t < a.T && d < D)
+        rx[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) +
+                                                ((size_t)t * D + d) * (XBF16 ? 2 : 4));
+    }
+    const int nw = min(DK, D - d0) * E;  // valid floats of this chunk
+    const float* wsrc = a.W_r + (size_t)d0 * E;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      const int f = 4 * (tid + 256 * i);
+      float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (wvec) {
+        if (f < nw) w4 = *reinterpret_cast<const float4*>(wsrc + f);
+      } else {
+        if (f < nw) w4.x = wsrc[f];
+        if (f + 1 < nw) w4.y = wsrc[f + 1];
+        if (f + 2 < nw) w4.z = wsrc[f + 2];
+        if (f + 3 < nw) w4.w = wsrc[f + 3];
       }
-      xs[dd][tl] = v;
+      rw[i] = w4;
     }
-    for (int q = tid; q < DK * EP; q += 256) {
-      const int dd = q / EP, e = q % EP;
-      float v = 0.0f;
-      if (dd < dk && e < a.E) v = a.W_r[(size_t)(d0 + dd) * a.E + e];
-      wsm[dd][e] = v;
+  };
+  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NXV; ++i) {
+      const int v = tid + 256 * i;
+      if (v < TB * DK / VX) {
+        const int tl = v / (DK / VX), dg = v % (DK / VX);
+        const uint32_t w4[4] = {rx[i].x, rx[i].y, rx[i].z, rx[i].w};
+#pragma unroll
+        for (int q = 0; q < VX; ++q) {
+          const float val = XBF16 ? __uint_as_float(((q & 1) ? (w4[q >> 1] & 0xFFFF0000u) : (w4[q >> 1] << 16)))
+                                  : __uint_as_float(w4[q]);
+          xs[buf][VX * dg + q][tl] = val;
+        }
+      }
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      const int f = 4 * (tid + 256 * i);
+      const float vals[4] = {rw[i].x, rw[i].y, rw[i].z, rw[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ff = f + q;
+        const int dd = ff / E, e = ff % E;
+        if (dd < DK) wsm[buf][dd][e] = vals[q];
+      }
+    }
+  };
+
+  const int nch = (D + DK - 1) / DK;
+  // padded experts (E <= e < EP) read zeros: clear those LDS columns once
+  for (int q = tid; q < 2 * DK * EP; q += 256) (&wsm[0][0][0])[q] = 0.0f;
+  __syncthreads();
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load_chunk(c + 1);
+    const int dk = min(DK, D - c * DK);
     for (int dd = 0; dd < dk; ++dd) {
       float xv[RT], wv[RE];
 #pragma unroll
-      for (int i = 0; i < RT; ++i) xv[i] = xs[dd][tt * RT + i];
+      for (int i = 0; i < RT; ++i) xv[i] = xs[buf][dd][tt * RT + i];
 #pragma unroll
-      for (int j = 0; j < RE; ++j) wv[j] = wsm[dd][te + NE * j];
+      for (int j = 0; j < RE; ++j) wv[j] = wsm[buf][dd][te + NE * j];
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int j = 0; j < RE; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
     }
+    if (c + 1 < nch) store_chunk(buf ^ 1);
+    __syncthreads();
   }
+
+  // Logits of the workgroup's tokens to LDS ([token][expert], reusing the
+  // W_r buffers), so that the selection below can walk the tokens with a
+  // loop instead of unrolled register indexing.
+  static_assert(TB <= 2 * DK, "logit tile must fit in the W_r buffers");
+  float* lg = &wsm[0][0][0];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < RE; ++j) lg[(tt * RT + i) * EP + te + NE * j] = acc[i][j];
+  __syncthreads();
 
   for (int i = 0; i < RT; ++i) {
     const int t = t0 + tt * RT + i;
-    float key[RE];
+    const float* row = lg + (tt * RT + i) * EP;
+    float key[RE], lgt[RE];
     bool avail[RE];
 #pragma unroll
     for (int j = 0; j < RE; ++j) {
       const int e = te + NE * j;
       avail[j] = e < a.E;
-      key[j] = avail[j] ? acc[i][j] + (a.bias ? a.bias[e] : 0.0f) : -INFINITY;
-      if (a.logits && t < a.T && avail[j]) a.logits[(size_t)t * a.E + e] = acc[i][j];
+      lgt[j] = row[e];
+      key[j] = avail[j] ? lgt[j] + (a.bias ? a.bias[e] : 0.0f) : -INFINITY;
+      if (a.logits && t < a.T && avail[j]) a.logits[(size_t)t * a.E + e] = lgt[j];
     }
     // softmax normaliser over all experts: max key, then sum of exp(key - max)
     float m = -INFINITY;
@@ -128,7 +202,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
           if (avail[j] && (key[j] > bk || (key[j] == bk && e < bi))) {
             bk = key[j];
             bi = e;
-            bl = acc[i][j];
+            bl = lgt[j];
           }
         }
 #pragma unroll
@@ -188,10 +262,10 @@ hipError_t launch_router(const moe_cfg& c, const void* x, const float* W_r, cons
                          int32_t* idx, float* w, float* logits, hipStream_t s) {
   RouterArgs a{x, W_r, bias, idx, w, logits, c.T, c.D, c.E, c.top_k, c.gating, c.renorm};
   const bool b = c.act_dtype == MOE_BF16;
-  if (c.E <= 8) return launch<8, 1, 1, 32>(a, b, s);
-  if (c.E <= 16) return launch<16, 1, 2, 32>(a, b, s);
-  if (c.E <= 32) return launch<32, 1, 4, 32>(a, b, s);
-  if (c.E <= 64) return launch<64, 1, 8, 32>(a, b, s);
+  if (c.E <= 8) return launch<8, 1, 1, 256>(a, b, s);
+  if (c.E <= 16) return launch<16, 1, 2, 128>(a, b, s);
+  if (c.E <= 32) return launch<32, 1, 4, 64>(a, b, s);
+  if (c.E <= 64) return launch<64, 1, 8, 64>(a, b, s);
   if (c.E <= 128) return launch<64, 2, 8, 32>(a, b, s);
   if (c.E <= 256) return launch<64, 4, 8, 32>(a, b, s);
   if (c.E <= 384) return launch<64, 6, 16, 32>(a, b, s);
