@@ -39,10 +39,9 @@
 // other stage, and the global loads of steps kt+2 and kt+3 are in flight.
 // One barrier per 32-k step.
 //
-// Workgroup -> tile: tiles are numbered M-tile fastest, so consecutive tiles
-// share one weight N-tile; workgroup b runs on XCD (b mod 8), and b is
-// remapped so that each XCD takes a contiguous range of tiles and its L2
-// serves the weight tile to all of them.
+// Workgroup -> tile: workgroup b runs on XCD (b mod 8), and b is remapped so
+// that each XCD takes a contiguous range of the tile order (tile_of), whose
+// neighbours share weight and activation slabs in that XCD's L2.
 #include "common.h"
 #include "launch.h"
 
@@ -146,6 +145,19 @@ __device__ __forceinline__ void store_b_mx(unsigned char* Bs, u32x4_t codes, uin
   }
 }
 
+// Tile order: N-tiles in groups of 4; inside a group, M-tile major and the
+// 4 N-tiles minor. The 32 workgroups an XCD runs at once then cover about
+// 8 M-tiles x 4 N-tiles (one expert's weight columns), so its L2 serves each
+// weight slab to ~8 workgroups and each x_perm slab to 4.
+__device__ __forceinline__ void tile_of(int L, int MT, int NT, int& mt, int& nt) {
+  constexpr int G = 4;
+  const int g = L / (MT * G);
+  const int rem = L - g * MT * G;
+  const int gs = min(G, NT - g * G);
+  mt = rem / gs;
+  nt = g * G + rem % gs;
+}
+
 template <int MODE, bool MX>
 __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE * STAGE];
@@ -158,8 +170,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
   const int b = blockIdx.x;
   const int L = (b & 7) * a.per_xcd + (b >> 3);
   if (L >= a.max_tiles * a.n_tiles_n) return;
-  const int mt = L % a.max_tiles;
-  const int nt = L / a.max_tiles;
+  int mt, nt;
+  tile_of(L, a.max_tiles, a.n_tiles_n, mt, nt);
   int e, row0, row_end;
   if (a.tilemap) {
     if (mt >= a.tilemap[0]) return;
@@ -439,6 +451,257 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 weights: 8 waves (two per SIMD), asynchronous global->LDS copies.
+//
+// Each wave computes 128 rows x 64 B-columns (4 x 2 MFMA tiles, 128 fp32
+// accumulators), so two waves share each SIMD and one's LDS waits are
+// covered by the other's MFMAs. SwiGLU: wave w owns f = 32w..32w+31 of the
+// tile, i.e. gate B-column 32w + l and up B-column 256 + 32w + l.
+// Global data goes straight to LDS with global_load_lds_dwordx4 (no
+// register staging), NSTAGE_DMA stages deep: the copies of step kt+3 are
+// issued after the barrier of step kt. The compiler cannot tell that the
+// transposing LDS reads touch only completed copies, so those reads are
+// written as one asm block that also waits for them; completion of the
+// copies is tracked with explicit vmcnt waits before each barrier.
+constexpr int NSTAGE_DMA = 4;  // 4 x 40 KB = 160 KB of LDS
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
+}
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE_DMA * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;  // 0..7
+
+  const int b = blockIdx.x;
+  const int L = (b & 7) * a.per_xcd + (b >> 3);
+  if (L >= a.max_tiles * a.n_tiles_n) return;
+  int mt, nt;
+  tile_of(L, a.max_tiles, a.n_tiles_n, mt, nt);
+  int e, row0, row_end;
+  if (a.tilemap) {
+    if (mt >= a.tilemap[0]) return;
+    e = a.tilemap[1 + 2 * mt];
+    row0 = a.tilemap[2 + 2 * mt];
+    row_end = a.offsets[e + 1];
+  } else {
+    e = 0;
+    row0 = mt * BM;
+    if (row0 >= a.rows) return;
+    row_end = a.rows;
+  }
+  const int K = a.K, N = a.N;
+  const int n0 = MODE == MODE_SWIGLU ? nt * 256 : nt * 512;
+  const int nk = K / BK;
+
+  // ---- A copies: LDS entry p = 4m + s (16 bytes) holds k-group s ^ swz4(m)
+  // of row m; wave w's copy fills entries 64w..64w+63, lane l entry 64w + l.
+  const uint16_t* a_g;
+  {
+    const int p = tid, m = p >> 2, q = (p & 3) ^ swz4(p >> 2);
+    a_g = a.A + (size_t)min(row0 + m, row_end - 1) * K + 8 * q;
+  }
+  // ---- B copies: LDS row k (1 KB) slot c holds 8-column chunk
+  // c ^ (4*(k & 3)); wave w copies rows 4w..4w+3, lane l slot l.
+  const uint16_t* b_g[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane ^ (4 * i);  // k & 3 == i for row 4w + i
+    int col;
+    const uint16_t* base;
+    if (MODE == MODE_SWIGLU) {
+      col = n0 + 8 * (c & 31);
+      base = static_cast<const uint16_t*>(c >= 32 ? a.B1 : a.B0);
+    } else {
+      col = n0 + 8 * c;
+      base = static_cast<const uint16_t*>(a.B0);
+    }
+    if (col + 8 > N) col = 0;  // columns past N: any valid data, never stored
+    b_g[i] = base + ((size_t)e * K + 4 * wave + i) * N + col;
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    unsigned char* As = smem + (kt % NSTAGE_DMA) * STAGE;
+    unsigned char* Bs = As + A_STAGE;
+    const int k0 = kt * BK;
+    dma16(a_g + k0, As + wave * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(b_g[i] + (size_t)k0 * N, Bs + (4 * wave + i) * 1024);
+  };
+  constexpr int PER = 5;  // copies per thread per stage
+
+  // wave's B-column bases: j = 0 gate (or first half), j = 1 up (second)
+  int bcol[2];
+  if (MODE == MODE_SWIGLU) {
+    bcol[0] = 32 * wave;
+    bcol[1] = 256 + 32 * wave;
+  } else {
+    bcol[0] = 64 * wave;
+    bcol[1] = 64 * wave + 32;
+  }
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int lrow = lane & 31;
+  const int lq = lane >> 5;
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // per-lane LDS byte offsets of the transposed B reads (k-step 0, rows
+  // 8*lq + tr_row and +4) for the two B fragments
+  uint32_t tr_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = bcol[j] + tr_col;
+    const int r0 = 8 * lq + tr_row;  // r0 & 3 == tr_row
+    tr_off[j] = A_STAGE + r0 * 1024 + ((col >> 3) ^ (4 * tr_row)) * 16 + (col & 7) * 2;
+  }
+
+#pragma unroll
+  for (int s = 0; s < NSTAGE_DMA - 1; ++s)
+    if (s < nk) issue(s);
+
+  // One 32-k step on LDS stage S (a compile-time constant in the unrolled
+  // main loop, so LDS addresses are a register plus an immediate).
+#define MOE_STEP(S)                                                                        \
+  do {                                                                                     \
+    /* this thread's copies of stage kt have landed (later ones may fly) */                \
+    const int ahead = min(NSTAGE_DMA - 2, nk - 1 - kt);                                    \
+    if (ahead >= 2) wait_vmcnt<2 * PER>();                                                 \
+    else if (ahead == 1) wait_vmcnt<PER>();                                                \
+    else wait_vmcnt<0>();                                                                  \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                     \
+    __builtin_amdgcn_s_barrier();                                                          \
+    asm volatile("" ::: "memory");                                                         \
+    if (kt + NSTAGE_DMA - 1 < nk) issue(kt + NSTAGE_DMA - 1);                              \
+    const unsigned char* As = smem + (S) * STAGE;                                          \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                     \
+      const int q = 2 * kk + lq;                                                           \
+      bf16x8_t af[4], bfr[2];                                                              \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+        const int m = 32 * i + lrow;                                                       \
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + m * 64 + ((q ^ swz4(m)) * 16));    \
+      }                                                                                    \
+      s16x4_t h00, h01, h10, h11;                                                          \
+      const uint32_t ad0 = smem_addr + (S) * STAGE + tr_off[0] + kk * 16 * 1024;           \
+      const uint32_t ad1 = smem_addr + (S) * STAGE + tr_off[1] + kk * 16 * 1024;           \
+      asm volatile(                                                                        \
+          "ds_read_b64_tr_b16 %0, %4\n\t"                                                  \
+          "ds_read_b64_tr_b16 %1, %4 offset:4096\n\t"                                      \
+          "ds_read_b64_tr_b16 %2, %5\n\t"                                                  \
+          "ds_read_b64_tr_b16 %3, %5 offset:4096\n\t"                                      \
+          "s_waitcnt lgkmcnt(0)"                                                           \
+          : "=&v"(h00), "=&v"(h01), "=&v"(h10), "=&v"(h11)                                 \
+          : "v"(ad0), "v"(ad1)                                                             \
+          : "memory");                                                                     \
+      {                                                                                    \
+        const s16x8_t hv = {h00[0], h00[1], h00[2], h00[3], h01[0], h01[1], h01[2], h01[3]}; \
+        bfr[0] = __builtin_bit_cast(bf16x8_t, hv);                                         \
+      }                                                                                    \
+      {                                                                                    \
+        const s16x8_t hv = {h10[0], h10[1], h10[2], h10[3], h11[0], h11[1], h11[2], h11[3]}; \
+        bfr[1] = __builtin_bit_cast(bf16x8_t, hv);                                         \
+      }                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                        \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);  \
+    }                                                                                      \
+  } while (0)
+
+  static_assert(NSTAGE_DMA == 4, "the step loop below is unrolled for 4 stages");
+  const uint32_t smem_addr = lds_addr(smem);
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    MOE_STEP(0);
+    ++kt;
+    MOE_STEP(1);
+    ++kt;
+    MOE_STEP(2);
+    ++kt;
+    MOE_STEP(3);
+    kt -= 3;
+  }
+  // the last nk % 4 steps (only when K is not a multiple of 128)
+  for (; kt < nk; ++kt) {
+    const int st = kt & 3;
+    MOE_STEP(st);
+  }
+#undef MOE_STEP
+
+  // ---- epilogue through LDS, so that global stores are 16 bytes per lane.
+  // Accumulator r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of
+  // its 32x32 tile.
+  __syncthreads();  // every wave is done with the operand stages
+  if (MODE == MODE_SWIGLU) {
+    // wave tile: 128 rows x 32 f of bf16 h = SiLU(clamp(g)) * clamp(u)
+    unsigned char* wl = smem + wave * (128 * 64);
+    const bool clampit = a.clamp > 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * i + 8 * (r >> 2) + 4 * lq + (r & 3);
+        float g = acc[i][0][r], u = acc[i][1][r];
+        if (clampit) {
+          g = clampf(g, a.clamp);
+          u = clampf(u, a.clamp);
+        }
+        *reinterpret_cast<uint16_t*>(wl + m * 64 + lrow * 2) =
+            static_cast<uint16_t>(f32_to_bf16(silu_f32(g) * u));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own wave's tile only
+    uint16_t* H = static_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane, m = idx >> 2, ch = idx & 3;
+      const int grow = row0 + m, f = n0 + 32 * wave + 8 * ch;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 64 + ch * 16);
+      if (grow < row_end && f < N) *reinterpret_cast<u32x4_t*>(H + (size_t)grow * N + f) = v;
+    }
+  } else {
+    // wave tile: 128 rows x 64 fp32 columns, in two halves of 32 columns
+    unsigned char* wl = smem + wave * (128 * 128);
+    float* Y = static_cast<float*>(a.out);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 32 * i + 8 * (r >> 2) + 4 * lq + (r & 3);
+          *reinterpret_cast<float*>(wl + m * 128 + lrow * 4) = acc[i][j][r];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int idx = it * 64 + lane, m = idx >> 3, ch = idx & 7;
+        const int grow = row0 + m, n = n0 + bcol[j] + 4 * ch;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 128 + ch * 16);
+        if (grow < row_end && n < N) *reinterpret_cast<u32x4_t*>(Y + (size_t)grow * N + n) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half overwrites
+    }
+  }
+}
+
 hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   Args a;
@@ -461,10 +724,10 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   const dim3 grid(8 * a.per_xcd);
   if (mode == MODE_SWIGLU) {
     if (p.mxfp4) gemm_kernel<MODE_SWIGLU, true><<<grid, 256, 0, s>>>(a);
-    else gemm_kernel<MODE_SWIGLU, false><<<grid, 256, 0, s>>>(a);
+    else gemm_bf16_kernel<MODE_SWIGLU><<<grid, 512, 0, s>>>(a);
   } else {
     if (p.mxfp4) gemm_kernel<MODE_DOWN, true><<<grid, 256, 0, s>>>(a);
-    else gemm_kernel<MODE_DOWN, false><<<grid, 256, 0, s>>>(a);
+    else gemm_bf16_kernel<MODE_DOWN><<<grid, 512, 0, s>>>(a);
   }
   return hipGetLastError();
 }
