@@ -2,7 +2,7 @@
 //
 // "ops-transformer MoE operator on Ascend NPU", optimisation 3: all experts'
 // matmuls in one launch although each expert has a different number of
-// rows. The tile map lists every (expert, first row) M-tile of kBM rows over
+// rows. The tile map lists every (expert, first row) M-tile of BM rows over
 // the kept segments; the GEMM grid is sized on the host for the worst case
 // and surplus workgroups exit, so no count travels back to the host.
 //
@@ -17,7 +17,7 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int32_t* __restrict__ tilemap) {
+                                                       int bm, int32_t* __restrict__ tilemap) {
   __shared__ int wave_tot[16];
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6;
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
     start = offsets[e];
     rows = offsets[e + 1] - start;
   }
-  const int nt = (rows + kBM - 1) / kBM;
+  const int nt = (rows + bm - 1) / bm;
   const int incl = wave_inclusive_scan(nt);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
   for (int w = 0; w < wave; ++w) base += wave_tot[w];
   for (int i = 0; i < nt; ++i) {
     tilemap[1 + 2 * (base + i)] = e;
-    tilemap[2 + 2 * (base + i)] = start + i * kBM;
+    tilemap[2 + 2 * (base + i)] = start + i * bm;
   }
   if (e == 1023) tilemap[0] = base + nt;
 }
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restri
 
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
                           hipStream_t s) {
-  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, tilemap);
+  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, gemm_bm(c), tilemap);
   return hipGetLastError();
 }
 

@@ -452,19 +452,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 weights: 8 waves (two per SIMD), asynchronous global->LDS copies.
+// bf16 weights: 256 x 256 tiles, 8 waves (two per SIMD), asynchronous
+// global->LDS copies.
 //
+// Tile: 256 rows x 256 B-columns x 32 k per stage (SwiGLU: 128 gate and
+// the same 128 up columns). A square tile moves the fewest bytes per flop
+// that 64K fp32 accumulators per CU allow: 32 KB per 32-k step for 4.2 MFLOP.
 // Each wave computes 128 rows x 64 B-columns (4 x 2 MFMA tiles, 128 fp32
 // accumulators), so two waves share each SIMD and one's LDS waits are
-// covered by the other's MFMAs. SwiGLU: wave w owns f = 32w..32w+31 of the
-// tile, i.e. gate B-column 32w + l and up B-column 256 + 32w + l.
+// covered by the other's MFMAs. SwiGLU: wave (wm, wn) owns rows
+// 128wm..128wm+127 and f = 32wn..32wn+31, i.e. gate B-column 32wn + l and
+// up B-column 128 + 32wn + l.
 // Global data goes straight to LDS with global_load_lds_dwordx4 (no
 // register staging), NSTAGE_DMA stages deep: the copies of step kt+3 are
 // issued after the barrier of step kt. The compiler cannot tell that the
 // transposing LDS reads touch only completed copies, so those reads are
 // written as one asm block that also waits for them; completion of the
 // copies is tracked with explicit vmcnt waits before each barrier.
-constexpr int NSTAGE_DMA = 4;  // 4 x 40 KB = 160 KB of LDS
+constexpr int BM2 = kBM_BF16;       // 256
+constexpr int BN2 = 256;            // B-columns per tile
+constexpr int A_STAGE2 = BM2 * BK * 2;   // 16 KB
+constexpr int B_STAGE2 = BN2 * BK * 2;   // 16 KB
+constexpr int STAGE2 = A_STAGE2 + B_STAGE2;
+constexpr int NSTAGE_DMA = 4;       // 4 x 32 KB = 128 KB of LDS
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -480,11 +490,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE_DMA * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE_DMA * STAGE2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;  // 0..7
+  const int wm = wave >> 2;   // row half
+  const int wn = wave & 3;    // column quarter
 
   const int b = blockIdx.x;
   const int L = (b & 7) * a.per_xcd + (b >> 3);
@@ -499,57 +511,61 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
     row_end = a.offsets[e + 1];
   } else {
     e = 0;
-    row0 = mt * BM;
+    row0 = mt * BM2;
     if (row0 >= a.rows) return;
     row_end = a.rows;
   }
   const int K = a.K, N = a.N;
-  const int n0 = MODE == MODE_SWIGLU ? nt * 256 : nt * 512;
+  const int n0 = MODE == MODE_SWIGLU ? nt * 128 : nt * 256;
   const int nk = K / BK;
 
   // ---- A copies: LDS entry p = 4m + s (16 bytes) holds k-group s ^ swz4(m)
-  // of row m; wave w's copy fills entries 64w..64w+63, lane l entry 64w + l.
-  const uint16_t* a_g;
-  {
-    const int p = tid, m = p >> 2, q = (p & 3) ^ swz4(p >> 2);
-    a_g = a.A + (size_t)min(row0 + m, row_end - 1) * K + 8 * q;
-  }
-  // ---- B copies: LDS row k (1 KB) slot c holds 8-column chunk
-  // c ^ (4*(k & 3)); wave w copies rows 4w..4w+3, lane l slot l.
-  const uint16_t* b_g[4];
+  // of row m; copy r of wave w fills entries 512r + 64w .. +63.
+  const uint16_t* a_g[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = lane ^ (4 * i);  // k & 3 == i for row 4w + i
+  for (int r = 0; r < 2; ++r) {
+    const int p = 512 * r + tid, m = p >> 2, q = (p & 3) ^ swz4(m);
+    a_g[r] = a.A + (size_t)min(row0 + m, row_end - 1) * K + 8 * q;
+  }
+  // ---- B copies: LDS k-row (512 bytes = 32 chunks of 8 columns) slot c
+  // holds chunk c ^ (4*(k & 3)); copy r of wave w fills rows 4w + 2r and
+  // 4w + 2r + 1 (lanes 0-31 and 32-63).
+  const uint16_t* b_g[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = 4 * wave + 2 * r + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (k & 3));
     int col;
     const uint16_t* base;
     if (MODE == MODE_SWIGLU) {
-      col = n0 + 8 * (c & 31);
-      base = static_cast<const uint16_t*>(c >= 32 ? a.B1 : a.B0);
+      col = n0 + 8 * (c & 15);
+      base = static_cast<const uint16_t*>(c >= 16 ? a.B1 : a.B0);
     } else {
       col = n0 + 8 * c;
       base = static_cast<const uint16_t*>(a.B0);
     }
     if (col + 8 > N) col = 0;  // columns past N: any valid data, never stored
-    b_g[i] = base + ((size_t)e * K + 4 * wave + i) * N + col;
+    b_g[r] = base + ((size_t)e * K + k) * N + col;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    unsigned char* As = smem + (kt % NSTAGE_DMA) * STAGE;
-    unsigned char* Bs = As + A_STAGE;
+    unsigned char* As = smem + (kt % NSTAGE_DMA) * STAGE2;
+    unsigned char* Bs = As + A_STAGE2;
     const int k0 = kt * BK;
-    dma16(a_g + k0, As + wave * 1024);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_g[i] + (size_t)k0 * N, Bs + (4 * wave + i) * 1024);
+    dma16(a_g[0] + k0, As + wave * 1024);
+    dma16(a_g[1] + k0, As + 8192 + wave * 1024);
+    dma16(b_g[0] + (size_t)k0 * N, Bs + (4 * wave) * 512);
+    dma16(b_g[1] + (size_t)k0 * N, Bs + (4 * wave + 2) * 512);
   };
-  constexpr int PER = 5;  // copies per thread per stage
+  constexpr int PER = 4;  // copies per thread per stage
 
   // wave's B-column bases: j = 0 gate (or first half), j = 1 up (second)
   int bcol[2];
   if (MODE == MODE_SWIGLU) {
-    bcol[0] = 32 * wave;
-    bcol[1] = 256 + 32 * wave;
+    bcol[0] = 32 * wn;
+    bcol[1] = 128 + 32 * wn;
   } else {
-    bcol[0] = 64 * wave;
-    bcol[1] = 64 * wave + 32;
+    bcol[0] = 64 * wn;
+    bcol[1] = 64 * wn + 32;
   }
 
   f32x16_t acc[4][2];
@@ -571,7 +587,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
   for (int j = 0; j < 2; ++j) {
     const int col = bcol[j] + tr_col;
     const int r0 = 8 * lq + tr_row;  // r0 & 3 == tr_row
-    tr_off[j] = A_STAGE + r0 * 1024 + ((col >> 3) ^ (4 * tr_row)) * 16 + (col & 7) * 2;
+    tr_off[j] = A_STAGE2 + r0 * 512 + ((col >> 3) ^ (4 * tr_row)) * 16 + (col & 7) * 2;
   }
 
 #pragma unroll
@@ -591,22 +607,22 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
     __builtin_amdgcn_s_barrier();                                                          \
     asm volatile("" ::: "memory");                                                         \
     if (kt + NSTAGE_DMA - 1 < nk) issue(kt + NSTAGE_DMA - 1);                              \
-    const unsigned char* As = smem + (S) * STAGE;                                          \
+    const unsigned char* As = smem + (S) * STAGE2;                                         \
     _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                     \
       const int q = 2 * kk + lq;                                                           \
       bf16x8_t af[4], bfr[2];                                                              \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-        const int m = 32 * i + lrow;                                                       \
+        const int m = 128 * wm + 32 * i + lrow;                                            \
         af[i] = *reinterpret_cast<const bf16x8_t*>(As + m * 64 + ((q ^ swz4(m)) * 16));    \
       }                                                                                    \
       s16x4_t h00, h01, h10, h11;                                                          \
-      const uint32_t ad0 = smem_addr + (S) * STAGE + tr_off[0] + kk * 16 * 1024;           \
-      const uint32_t ad1 = smem_addr + (S) * STAGE + tr_off[1] + kk * 16 * 1024;           \
+      const uint32_t ad0 = smem_addr + (S) * STAGE2 + tr_off[0] + kk * 16 * 512;           \
+      const uint32_t ad1 = smem_addr + (S) * STAGE2 + tr_off[1] + kk * 16 * 512;           \
       asm volatile(                                                                        \
           "ds_read_b64_tr_b16 %0, %4\n\t"                                                  \
-          "ds_read_b64_tr_b16 %1, %4 offset:4096\n\t"                                      \
+          "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"                                      \
           "ds_read_b64_tr_b16 %2, %5\n\t"                                                  \
-          "ds_read_b64_tr_b16 %3, %5 offset:4096\n\t"                                      \
+          "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"                                      \
           "s_waitcnt lgkmcnt(0)"                                                           \
           : "=&v"(h00), "=&v"(h01), "=&v"(h10), "=&v"(h11)                                 \
           : "v"(ad0), "v"(ad1)                                                             \
@@ -672,7 +688,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int idx = it * 64 + lane, m = idx >> 2, ch = idx & 3;
-      const int grow = row0 + m, f = n0 + 32 * wave + 8 * ch;
+      const int grow = row0 + 128 * wm + m, f = n0 + 32 * wn + 8 * ch;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 64 + ch * 16);
       if (grow < row_end && f < N) *reinterpret_cast<u32x4_t*>(H + (size_t)grow * N + f) = v;
     }
@@ -693,7 +709,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int idx = it * 64 + lane, m = idx >> 3, ch = idx & 7;
-        const int grow = row0 + m, n = n0 + bcol[j] + 4 * ch;
+        const int grow = row0 + 128 * wm + m, n = n0 + bcol[j] + 4 * ch;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 128 + ch * 16);
         if (grow < row_end && n < N) *reinterpret_cast<u32x4_t*>(Y + (size_t)grow * N + n) = v;
       }
@@ -712,7 +728,10 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   a.max_tiles = p.max_tiles;
   a.K = p.K;
   a.N = p.N;
-  a.n_tiles_n = mode == MODE_SWIGLU ? ceil_div(p.N, 256) : ceil_div(p.N, 512);
+  if (p.mxfp4)
+    a.n_tiles_n = mode == MODE_SWIGLU ? ceil_div(p.N, 256) : ceil_div(p.N, 512);
+  else
+    a.n_tiles_n = mode == MODE_SWIGLU ? ceil_div(p.N, 128) : ceil_div(p.N, 256);
   const long long total = (long long)a.max_tiles * a.n_tiles_n;
   a.per_xcd = ceil_div(total, 8);
   a.B0 = p.B0;

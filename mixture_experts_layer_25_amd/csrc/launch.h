@@ -10,8 +10,10 @@
 
 namespace moe {
 
-// Rows per M-tile of the grouped GEMMs (both projections).
+// Rows per M-tile of the grouped GEMMs (both projections): 256 for bf16
+// weights, 128 for MXFP4 weights.
 constexpr int kBM = 128;
+constexpr int kBM_BF16 = 256;
 // Tokens per dispatch chunk (one workgroup of the count and rank kernels).
 constexpr int kChunk = 256;
 
@@ -20,7 +22,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Upper bound of the number of M-tiles: every kept row in a full tile plus
 // one partial tile per expert.
-inline int max_mtiles(const moe_cfg& c) { return ceil_div((long long)c.T * c.top_k, kBM) + c.E; }
+inline int gemm_bm(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? kBM_BF16 : kBM; }
+inline int max_mtiles(const moe_cfg& c) {
+  return ceil_div((long long)c.T * c.top_k, gemm_bm(c)) + c.E;
+}
 // int32 entries of the tile map: [0] = tile count, then (expert, row0) pairs.
 inline size_t tilemap_ints(const moe_cfg& c) { return 1 + 2 * (size_t)max_mtiles(c); }
 inline int num_chunks(const moe_cfg& c) { return ceil_div(c.T, kChunk); }
@@ -33,7 +38,8 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
                            int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,
                            int32_t* chunk_ws, hipStream_t s);
 
-// Builds the tile map (tilemap_ints(c) int32) from device offsets.
+// Builds the tile map (tilemap_ints(c) int32, M-tiles of gemm_bm(c) rows)
+// from device offsets.
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap, hipStream_t s);
 
 // bf16 activations: grouped MFMA GEMMs over the tile map. A dense launch
