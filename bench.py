@@ -29,6 +29,7 @@ METRIC = "MoE-layer tokens/s (1 GPU) + grouped-GEMM TFLOP/s as % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc", "gemm.hip")
 
@@ -43,12 +44,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/kernel_trace_<workload>.txt from a rocprofv3 --stats run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_traffic_<workload>.{json,txt} from two --pmc runs")
+    ap.add_argument("--profile-command", default="",
+                    help="the command that produced the profile, recorded in the summary")
     return ap.parse_args()
 
 
@@ -66,6 +72,111 @@ def algorithmic(cfg, A):
     )
 
 
+CSRC = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc")
+
+
+def roofline_kernel(cfg):
+    """The gate/up kernel the workload's weight type selects, its source
+    file and what bounds it."""
+    if cfg.wdt == 0:
+        return {"name": "ffn_f32_gateup_kernel", "src": "ffn_f32.hip", "bound": "alu"}
+    if cfg.wdt == 2:
+        return {"name": "gemm_kernel<0, true>", "src": "gemm.hip", "bound": "mfma"}
+    return {"name": "gemm_bf16_kernel<0>", "src": "gemm.hip", "bound": "mfma"}
+
+
+def src_sha256(name):
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
+
+
+def short_name(n):
+    n = n.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    if "(" in n and not n.startswith("__"):
+        n = n[:n.index("(")]
+    return n[:90]
+
+
+def read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def find_one(d, suffix):
+    hits = [os.path.join(r, f) for r, _, fs in os.walk(d) for f in fs if f.endswith(suffix)]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one *{suffix} under {d}, found {len(hits)}")
+    return hits[0]
+
+
+def summarize_trace(run_dir, workload, command):
+    """rocprofv3 --kernel-trace --stats output -> profiles/kernel_trace_<workload>.txt"""
+    rows = read_csv(find_one(run_dir, "kernel_stats.csv"))
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.txt")
+    lines = [f"# rocprofv3 kernel-trace summary, workload {workload}",
+             f"# command: {command}",
+             "# durations in microseconds per dispatch",
+             f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{short_name(r['Name']):90s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, command):
+    """Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+    `bench.py --copy-calibration` -> HBM bytes per dispatch of each kernel.
+    Each counter is scaled by what it reads for the plain 256 MiB device copy
+    in the same run (the largest __amd_rocclr_copyBuffer dispatch), so
+    bytes = KiB x 1024 x (256 MiB / copy reading)."""
+    from collections import defaultdict
+    cfg_name = workload
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in read_csv(find_one(d, "counter_collection.csv"))
+                if r["Counter_Name"] == counter]
+        copy = max((float(r["Counter_Value"]) for r in rows
+                    if r["Kernel_Name"] == "__amd_rocclr_copyBuffer"), default=0.0)
+        if copy <= 0:
+            raise SystemExit(f"{counter}: no calibration copy in {d}")
+        scale = 256 * 1024 / copy
+        per = defaultdict(list)
+        for r in rows:
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        res[counter] = {"copy_kib": copy, "scale": scale,
+                        "kib_per_dispatch": {k: sum(v) / len(v) for k, v in per.items()}}
+    from mixture_experts_layer_25_amd import synthetic as syn
+    rk = roofline_kernel(syn.CONFIGS[cfg_name])
+    f = res["FETCH_SIZE"]
+    w = res["WRITE_SIZE"]
+
+    def nbytes(k):
+        return (f["kib_per_dispatch"].get(k, 0.0) * f["scale"]
+                + w["kib_per_dispatch"].get(k, 0.0) * w["scale"]) * 1024
+
+    rec = {"workload": cfg_name, "kernel": rk["name"], "kernel_src": rk["src"],
+           "kernel_src_sha256": src_sha256(rk["src"]),
+           "fetch_scale": f["scale"], "write_scale": w["scale"],
+           "bytes_per_launch": nbytes(rk["name"]), "command": command,
+           "per_kernel_bytes": {k: nbytes(k) for k in sorted(set(f["kib_per_dispatch"]) |
+                                                              set(w["kib_per_dispatch"]))}}
+    base = os.path.join(ROOT, "profiles", f"hbm_traffic_{cfg_name}")
+    json.dump(rec, open(base + ".json", "w"), indent=1)
+    lines = [f"# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, workload {cfg_name}",
+             f"# command: {command}",
+             f"# scaling: FETCH_SIZE x {f['scale']:.4f} (copy of 256 MiB read {f['copy_kib']:.1f} KiB), "
+             f"WRITE_SIZE x {w['scale']:.4f} (copy wrote {w['copy_kib']:.1f} KiB)",
+             f"# source sha256 of {rk['src']}: {rec['kernel_src_sha256']}",
+             f"{'kernel':90s} {'fetch_KiB':>12s} {'write_KiB':>12s} {'scaled_MB':>10s}"]
+    for k, b in rec["per_kernel_bytes"].items():
+        lines.append(f"{k:90s} {f['kib_per_dispatch'].get(k, 0.0):12.1f} "
+                     f"{w['kib_per_dispatch'].get(k, 0.0):12.1f} {b / 1e6:10.2f}")
+    open(base + ".txt", "w").write("\n".join(lines) + "\n")
+    print(base + ".json")
+
+
 def pct(vals, q):
     v = sorted(vals)
     i = min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))
@@ -74,6 +185,10 @@ def pct(vals, q):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.workload, args.profile_command)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.workload, args.profile_command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the layer on one GPU only (asked for --gpus {args.gpus}, "
@@ -106,33 +221,10 @@ def main():
         moe.forward(c, x, W_r, bias, w, y=y, ws=ws, topk_idx=idx, topk_w=tw, counts=counts,
                     offsets=offsets, wstruct=wstruct)
 
-    # ---------------- whole-layer timing
-    for _ in range(args.warmup):
-        fwd()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    all0, all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    all0.record()
-    for s, e in ev:
-        s.record()
-        fwd()
-        e.record()
-    all1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = all0.elapsed_time(all1)
-    ms_step = ms_total / args.steps
-    per_step = [s.elapsed_time(e) for s, e in ev]
-    A = int(offsets[-1].item())
-    cnt = counts.cpu().numpy()
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
-        f"kept pairs {A}, per-expert counts {cnt.min()}..{cnt.max()}")
-
-    # ---------------- per-stage timing (same inputs, separate launches)
-    work = algorithmic(cfg, A)
+    # The timed step runs the layer through its stage entry points (the same
+    # kernels moe_forward launches, in the same order, on the same stream),
+    # with a HIP event between stages, so that each stage's duration inside
+    # the timed region is known.
     d_ws = moe.workspace(c, moe.WS_DISPATCH, dev)
     f_ws = moe.workspace(c, moe.WS_EXPERT_FFN, dev)
     tk = T * k
@@ -145,12 +237,11 @@ def main():
     if cfg.shared_F:
         Hs = torch.empty((T, cfg.shared_F), dtype=torch.bfloat16, device=dev)
         ys = torch.empty((T, cfg.D), dtype=torch.float32, device=dev)
-    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     import ctypes
     P = ctypes.byref
-    sp = moe._stream()
+    sp = moe._stream(stream)
 
     stages = {
         "route": lambda: L.moe_route(P(c), x.data_ptr(), W_r.data_ptr(),
@@ -175,26 +266,57 @@ def main():
         order = ["route", "dispatch", "gate_up", "down", "shared", "combine"]
     else:
         order = ["route", "dispatch", "gate_up", "down", "combine"]
-    stage_ms = {}
-    for name in order:
-        fn = stages[name]
-        for _ in range(3):
-            assert fn() == 0, name
-        torch.cuda.synchronize()
-        tot = 0.0
-        flushed = name in ("route", "dispatch", "combine")
-        for _ in range(args.stage_reps):
-            if flushed:
-                flush.zero_()   # evict the 256 MB MALL so HBM-bound stages read HBM
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            assert fn() == 0, name
-            e.record(stream)
-            e.synchronize()
-            tot += s.elapsed_time(e)
-        stage_ms[name] = tot / args.stage_reps
-    del flush
+    fns = [stages[n] for n in order]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        for i, fn in enumerate(fns):
+            rc = fn()
+            if rc != 0:
+                raise moe.MoEError(f"{order[i]}: status {rc}")
+            if evs is not None:
+                evs[i + 1].record(stream)
+
+    def new_event():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---------------- whole-layer timing (K steps, stage events inside)
+    for _ in range(args.warmup):
+        step()
+    ev = [[new_event() for _ in range(len(order) + 1)] for _ in range(args.steps)]
+    all0, all1 = new_event(), new_event()
     torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    all0.record(stream)
+    for evs in ev:
+        step(evs)
+    all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = all0.elapsed_time(all1)
+    ms_step = ms_total / args.steps
+    per_step = [evs[0].elapsed_time(evs[-1]) for evs in ev]
+    stage_ms = {n: sum(evs[i].elapsed_time(evs[i + 1]) for evs in ev) / args.steps
+                for i, n in enumerate(order)}
+    A = int(offsets[-1].item())
+    cnt = counts.cpu().numpy()
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
+        f"kept pairs {A}, per-expert counts {cnt.min()}..{cnt.max()}")
+
+    # ---------------- the fused entry point, same inputs, for comparison
+    for _ in range(max(1, args.warmup // 2)):
+        fwd()
+    f0, f1 = new_event(), new_event()
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(args.steps):
+        fwd()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = f0.elapsed_time(f1) / args.steps
+    log(f"[bench] moe_forward: {fused_ms:.3f} ms/step")
+    work = algorithmic(cfg, A)
 
     if args.copy_calibration:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
@@ -212,7 +334,6 @@ def main():
     gu_tf = tfs(work["gate_up_flop"], stage_ms["gate_up"])
     dn_tf = tfs(work["down_flop"], stage_ms["down"])
     gemm_tf = tfs(work["gate_up_flop"] + work["down_flop"], stage_ms["gate_up"] + stage_ms["down"])
-    peak = PEAK_BF16_TFLOPS
     stage_report = {
         "route": {"ms": stage_ms["route"], "GB/s": gbs(work["route_bytes"], stage_ms["route"])},
         "dispatch": {"ms": stage_ms["dispatch"], "GB/s": gbs(work["dispatch_bytes"], stage_ms["dispatch"])},
@@ -225,21 +346,28 @@ def main():
                                   "TFLOP/s": tfs(work["shared_flop"], stage_ms["shared"])}
     for n in order:
         log(f"[bench] {n:9s} " + "  ".join(f"{kk} {vv:9.3f}" for kk, vv in stage_report[n].items()))
-    log(f"[bench] grouped GEMM {gemm_tf:.1f} TFLOP/s = {100 * gemm_tf / peak:.1f}% of bf16 peak")
+    log(f"[bench] grouped GEMM {gemm_tf:.1f} TFLOP/s = "
+        f"{100 * gemm_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
 
-    # HBM traffic of the dominant kernel from the committed counter summary
+    # Roofline of the dominant kernel: the grouped gate/up GEMM with the
+    # SwiGLU epilogue. Its duration is the mean of its event intervals inside
+    # the timed steps (the interval also holds the tiny tile-map kernel).
+    rk = roofline_kernel(cfg)
     traffic = None
     tf_path = TRAFFIC_FILE.format(workload=cfg.name)
     if os.path.exists(tf_path):
         rec = json.load(open(tf_path))
-        src_hash = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-        if rec.get("gemm_src_sha256") == src_hash:
-            traffic = rec.get("gate_up_bytes_per_launch")
-
-    roofline = {"bound": "mfma", "achieved": gu_tf, "peak": peak, "unit": "TFLOP/s",
+        if rec.get("kernel_src_sha256") == src_sha256(rk["src"]) and rec.get("kernel") == rk["name"]:
+            traffic = rec.get("bytes_per_launch")
+    if rk["bound"] == "alu":
+        peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
+    else:
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    roofline = {"bound": rk["bound"], "achieved": gu_tf, "peak": peak, "unit": unit,
                 "frac": gu_tf / peak, "traffic": traffic,
-                "kernel": "grouped gate/up GEMM + SwiGLU epilogue (gemm_kernel<SWIGLU>)",
-                "algorithmic": f"4*D*F per kept pair x {A} pairs = {work['gate_up_flop'] / 1e9:.1f} GFLOP"}
+                "kernel": rk["name"],
+                "algorithmic": f"4*D*F flop per kept (token, expert) pair x {A} pairs = "
+                               f"{work['gate_up_flop'] / 1e9:.3f} GFLOP per launch"}
 
     # ---------------- CPU oracle baseline (bounded sample)
     cpu = None
@@ -254,6 +382,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "fused_forward_ms_per_step": fused_ms,
         "p50_ms": pct(per_step, 50), "p95_ms": pct(per_step, 95), "p99_ms": pct(per_step, 99),
         "higher_is_better": True,
         "scaling": "weak",
@@ -265,7 +394,7 @@ def main():
                                f"{['fp32', 'bf16', 'mxfp4'][cfg.wdt]} weights",
                    "tokens": T, "kept_pairs": A, "seed": 0},
         "grouped_gemm_tflops": gemm_tf,
-        "grouped_gemm_frac_of_bf16_peak": gemm_tf / peak,
+        "grouped_gemm_frac_of_bf16_peak": gemm_tf / PEAK_BF16_TFLOPS,
         "stages": stage_report,
         "roofline": roofline,
         "cpu_baseline": cpu,
