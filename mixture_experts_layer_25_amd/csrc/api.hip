@@ -86,7 +86,19 @@ struct Carver {
 size_t dispatch_ws(const moe_cfg& c) {
   return moe::align_up((size_t)c.E * moe::num_chunks(c) * 4, kAlign);
 }
-size_t ffn_ws(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
+// expert FFN workspace: the tile map, then (bf16 weights) the split flags and
+// partial-sum slots of the grouped GEMMs
+size_t tilemap_bytes(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
+size_t ffn_ws(const moe_cfg& c) { return tilemap_bytes(c) + moe::split_bytes(c); }
+int32_t* split_flags_of(const moe_cfg& c, int32_t* tilemap) {
+  if (!moe::gemm_splits(c)) return nullptr;
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tilemap) + tilemap_bytes(c));
+}
+float* split_ws_of(const moe_cfg& c, int32_t* tilemap) {
+  if (!moe::gemm_splits(c)) return nullptr;
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(split_flags_of(c, tilemap)) +
+                                  moe::kSplitFlagBytes);
+}
 
 struct ForwardWs {
   int32_t *idx, *counts, *offsets, *slot_pos, *perm, *chunk_ws, *tilemap;
@@ -125,6 +137,8 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
   g.E = c.E;
   g.mxfp4 = c.w_dtype == MOE_MXFP4;
   g.clamp = c.clamp;
+  g.split_flags = split_flags_of(c, tilemap);
+  g.split_ws = split_ws_of(c, tilemap);
   return g;
 }
 
@@ -135,7 +149,7 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* offs
     return moe::launch_ffn_f32_gate_up(c, static_cast<const float*>(x_perm), offsets,
                                        static_cast<const float*>(w.W_gate),
                                        static_cast<const float*>(w.W_up), static_cast<float*>(H), s);
-  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, s);
+  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, split_flags_of(c, tilemap), s);
   if (e != hipSuccess) return e;
   moe::GemmProblem g = routed_problem(c, offsets, tilemap);
   g.A = x_perm;
@@ -157,7 +171,7 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
     return moe::launch_ffn_f32_down(c, static_cast<const float*>(H), offsets,
                                     static_cast<const float*>(w.W_down), y_perm, s);
   if (rebuild_map) {
-    hipError_t e = moe::launch_tilemap(c, offsets, tilemap, s);
+    hipError_t e = moe::launch_tilemap(c, offsets, tilemap, split_flags_of(c, tilemap), s);
     if (e != hipSuccess) return e;
   }
   moe::GemmProblem g = routed_problem(c, offsets, tilemap);

@@ -17,7 +17,8 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int bm, int32_t* __restrict__ tilemap) {
+                                                       int bm, int32_t* __restrict__ tilemap,
+                                                       int32_t* __restrict__ flags) {
   __shared__ int wave_tot[16];
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6;
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
     tilemap[2 + 2 * (base + i)] = start + i * bm;
   }
   if (e == 1023) tilemap[0] = base + nt;
+  if (flags && e < kSplitSlots) flags[e] = 0;
 }
 
 // expert of a segment row: the last e with offsets[e] <= r
@@ -98,8 +100,8 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
-                          hipStream_t s) {
-  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, gemm_bm(c), tilemap);
+                          int32_t* flags, hipStream_t s) {
+  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, gemm_bm(c), tilemap, flags);
   return hipGetLastError();
 }
 

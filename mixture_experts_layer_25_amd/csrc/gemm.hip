@@ -69,6 +69,8 @@ struct Args {
   const uint8_t* S1;
   float clamp;
   void* out;
+  float* split_ws;      // partial accumulators of split tiles (bf16 kernel), or nullptr
+  int32_t* split_flags; // one ready flag per partial slot, zero between launches
 };
 
 
@@ -464,17 +466,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(Args a) {
 // 128wm..128wm+127 and f = 32wn..32wn+31, i.e. gate B-column 32wn + l and
 // up B-column 128 + 32wn + l.
 // Global data goes straight to LDS with global_load_lds_dwordx4 (no
-// register staging), NSTAGE_DMA stages deep: the copies of step kt+3 are
-// issued after the barrier of step kt. The compiler cannot tell that the
-// transposing LDS reads touch only completed copies, so those reads are
-// written as one asm block that also waits for them; completion of the
-// copies is tracked with explicit vmcnt waits before each barrier.
+// register staging), NSTAGE_DMA stages deep: the copies of step kt+5 are
+// issued in the middle of step kt, right after the barrier that certifies
+// the copies of step kt+1 and that every wave is done reading stage kt.
+// Each 32-k step is two half-steps of 16 k; the MFMA fragments of a
+// half-step are read from LDS while the MFMAs of the previous half-step
+// run (two register sets), so LDS latency hides behind MFMA work.
 constexpr int BM2 = kBM_BF16;       // 256
 constexpr int BN2 = 256;            // B-columns per tile
 constexpr int A_STAGE2 = BM2 * BK * 2;   // 16 KB
 constexpr int B_STAGE2 = BN2 * BK * 2;   // 16 KB
 constexpr int STAGE2 = A_STAGE2 + B_STAGE2;
-constexpr int NSTAGE_DMA = 4;       // 4 x 32 KB = 128 KB of LDS
+constexpr int kCUsPerXCD = 32;      // MI355X: 256 CUs in 8 XCDs
+constexpr int kMaxSplit = 8;        // K-parts of a split tile
+constexpr int NSTAGE_DMA = 5;       // 5 x 32 KB = 160 KB, all of the LDS
+static_assert(NSTAGE_DMA >= 2 && NSTAGE_DMA <= 5, "copy waits are written for 2..5 stages");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -498,26 +504,52 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
   const int wm = wave >> 2;   // row half
   const int wn = wave & 3;    // column quarter
 
+  // ---- workgroup -> (tile, k-range). Workgroup b runs on XCD x = b mod 8
+  // as that XCD's i-th workgroup. The real tiles (M-tiles from the tile map
+  // x N-tiles, in tile_of order) are cut into 8 contiguous ranges, one per
+  // XCD. An XCD's whole rounds of kCUsPerXCD tiles run as whole tiles; the
+  // tiles of its last, partial round are each split along K into S parts
+  // (S x remainder <= kCUsPerXCD) so that the last round keeps every CU busy.
+  // Parts 0..S-2 leave fp32 partial sums in a workspace slot and raise its
+  // flag; part S-1 (the highest workgroup index of the tile, so the parts it
+  // waits for were dispatched before it) adds them in part order and runs
+  // the epilogue.
   const int b = blockIdx.x;
-  const int L = (b & 7) * a.per_xcd + (b >> 3);
-  if (L >= a.max_tiles * a.n_tiles_n) return;
+  const int xcd = b & 7, wi = b >> 3;
+  const int MT = a.tilemap ? a.tilemap[0] : a.max_tiles;
+  const int total = MT * a.n_tiles_n;
+  const int t_lo = (int)((long long)total * xcd / 8);
+  const int t_hi = (int)((long long)total * (xcd + 1) / 8);
+  const int whole = (t_hi - t_lo) / kCUsPerXCD * kCUsPerXCD;
+  const int rem = t_hi - t_lo - whole;
+  const int nk_all = a.K / BK;
+  int tile, S = 1, part = 0, slot0 = 0;
+  if (wi < whole) {
+    tile = t_lo + wi;
+  } else {
+    if (a.split_flags && rem > 0) S = min(min(kMaxSplit, kCUsPerXCD / rem), nk_all);
+    const int u = wi - whole;
+    if (u >= rem * S) return;
+    tile = t_lo + whole + u / S;
+    part = u % S;
+    slot0 = xcd * kCUsPerXCD + (u / S) * (S - 1);
+  }
   int mt, nt;
-  tile_of(L, a.max_tiles, a.n_tiles_n, mt, nt);
+  tile_of(tile, MT, a.n_tiles_n, mt, nt);
   int e, row0, row_end;
   if (a.tilemap) {
-    if (mt >= a.tilemap[0]) return;
     e = a.tilemap[1 + 2 * mt];
     row0 = a.tilemap[2 + 2 * mt];
     row_end = a.offsets[e + 1];
   } else {
     e = 0;
     row0 = mt * BM2;
-    if (row0 >= a.rows) return;
     row_end = a.rows;
   }
+  const int kt_begin = part * nk_all / S;
+  const int nk = (part + 1) * nk_all / S - kt_begin;
   const int K = a.K, N = a.N;
   const int n0 = MODE == MODE_SWIGLU ? nt * 128 : nt * 256;
-  const int nk = K / BK;
 
   // ---- A copies: LDS entry p = 4m + s (16 bytes) holds k-group s ^ swz4(m)
   // of row m; copy r of wave w fills entries 512r + 64w .. +63.
@@ -525,7 +557,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int p = 512 * r + tid, m = p >> 2, q = (p & 3) ^ swz4(m);
-    a_g[r] = a.A + (size_t)min(row0 + m, row_end - 1) * K + 8 * q;
+    a_g[r] = a.A + (size_t)min(row0 + m, row_end - 1) * K + kt_begin * BK + 8 * q;
   }
   // ---- B copies: LDS k-row (512 bytes = 32 chunks of 8 columns) slot c
   // holds chunk c ^ (4*(k & 3)); copy r of wave w fills rows 4w + 2r and
@@ -545,14 +577,27 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
       base = static_cast<const uint16_t*>(a.B0);
     }
     if (col + 8 > N) col = 0;  // columns past N: any valid data, never stored
-    b_g[r] = base + ((size_t)e * K + k) * N + col;
+    b_g[r] = base + ((size_t)e * K + kt_begin * BK + k) * N + col;
   }
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    unsigned char* As = smem + (kt % NSTAGE_DMA) * STAGE2;
+  // copies of step kt into the stage at byte offset `so`
+  auto issue = [&](int kt, uint32_t so) __attribute__((always_inline)) {
+    unsigned char* As = smem + so;
     unsigned char* Bs = As + A_STAGE2;
     const int k0 = kt * BK;
     dma16(a_g[0] + k0, As + wave * 1024);
     dma16(a_g[1] + k0, As + 8192 + wave * 1024);
+    dma16(b_g[0] + (size_t)k0 * N, Bs + (4 * wave) * 512);
+    dma16(b_g[1] + (size_t)k0 * N, Bs + (4 * wave + 2) * 512);
+  };
+  auto issue_a = [&](int kt, uint32_t so) __attribute__((always_inline)) {
+    unsigned char* As = smem + so;
+    const int k0 = kt * BK;
+    dma16(a_g[0] + k0, As + wave * 1024);
+    dma16(a_g[1] + k0, As + 8192 + wave * 1024);
+  };
+  auto issue_b = [&](int kt, uint32_t so) __attribute__((always_inline)) {
+    unsigned char* Bs = smem + so + A_STAGE2;
+    const int k0 = kt * BK;
     dma16(b_g[0] + (size_t)k0 * N, Bs + (4 * wave) * 512);
     dma16(b_g[1] + (size_t)k0 * N, Bs + (4 * wave + 2) * 512);
   };
@@ -578,88 +623,223 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
 
   const int lrow = lane & 31;
   const int lq = lane >> 5;
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // per-lane LDS byte offsets of the transposed B reads (k-step 0, rows
-  // 8*lq + tr_row and +4) for the two B fragments
-  uint32_t tr_off[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = bcol[j] + tr_col;
-    const int r0 = 8 * lq + tr_row;  // r0 & 3 == tr_row
-    tr_off[j] = A_STAGE2 + r0 * 512 + ((col >> 3) ^ (4 * tr_row)) * 16 + (col & 7) * 2;
-  }
-
-#pragma unroll
-  for (int s = 0; s < NSTAGE_DMA - 1; ++s)
-    if (s < nk) issue(s);
-
-  // One 32-k step on LDS stage S (a compile-time constant in the unrolled
-  // main loop, so LDS addresses are a register plus an immediate).
-#define MOE_STEP(S)                                                                        \
-  do {                                                                                     \
-    /* this thread's copies of stage kt have landed (later ones may fly) */                \
-    const int ahead = min(NSTAGE_DMA - 2, nk - 1 - kt);                                    \
-    if (ahead >= 2) wait_vmcnt<2 * PER>();                                                 \
-    else if (ahead == 1) wait_vmcnt<PER>();                                                \
-    else wait_vmcnt<0>();                                                                  \
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                     \
-    __builtin_amdgcn_s_barrier();                                                          \
-    asm volatile("" ::: "memory");                                                         \
-    if (kt + NSTAGE_DMA - 1 < nk) issue(kt + NSTAGE_DMA - 1);                              \
-    const unsigned char* As = smem + (S) * STAGE2;                                         \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                     \
-      const int q = 2 * kk + lq;                                                           \
-      bf16x8_t af[4], bfr[2];                                                              \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-        const int m = 128 * wm + 32 * i + lrow;                                            \
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + m * 64 + ((q ^ swz4(m)) * 16));    \
-      }                                                                                    \
-      s16x4_t h00, h01, h10, h11;                                                          \
-      const uint32_t ad0 = smem_addr + (S) * STAGE2 + tr_off[0] + kk * 16 * 512;           \
-      const uint32_t ad1 = smem_addr + (S) * STAGE2 + tr_off[1] + kk * 16 * 512;           \
-      asm volatile(                                                                        \
-          "ds_read_b64_tr_b16 %0, %4\n\t"                                                  \
-          "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"                                      \
-          "ds_read_b64_tr_b16 %2, %5\n\t"                                                  \
-          "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"                                      \
-          "s_waitcnt lgkmcnt(0)"                                                           \
-          : "=&v"(h00), "=&v"(h01), "=&v"(h10), "=&v"(h11)                                 \
-          : "v"(ad0), "v"(ad1)                                                             \
-          : "memory");                                                                     \
-      {                                                                                    \
-        const s16x8_t hv = {h00[0], h00[1], h00[2], h00[3], h01[0], h01[1], h01[2], h01[3]}; \
-        bfr[0] = __builtin_bit_cast(bf16x8_t, hv);                                         \
-      }                                                                                    \
-      {                                                                                    \
-        const s16x8_t hv = {h10[0], h10[1], h10[2], h10[3], h11[0], h11[1], h11[2], h11[3]}; \
-        bfr[1] = __builtin_bit_cast(bf16x8_t, hv);                                         \
-      }                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                        \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);  \
-    }                                                                                      \
-  } while (0)
-
-  static_assert(NSTAGE_DMA == 4, "the step loop below is unrolled for 4 stages");
   const uint32_t smem_addr = lds_addr(smem);
-  int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    MOE_STEP(0);
-    ++kt;
-    MOE_STEP(1);
-    ++kt;
-    MOE_STEP(2);
-    ++kt;
-    MOE_STEP(3);
-    kt -= 3;
+  // Per-lane LDS byte addresses, in stage 0, of the MFMA fragments.
+  //   A: row m = 128 wm + lrow, k-group 2 kk + lq of the 32-k step
+  //      (fragment i is 32 rows = 2048 bytes further).
+  //   B: transposed reads of k-rows 8 lq + tr_row and 8 lq + tr_row + 4
+  //      (2048 bytes apart) of the half-step kk (kk = 1 is 16 k-rows =
+  //      8192 bytes further), for the wave's two B-column bases.
+  uint32_t a_addr[2], b_addr[2];
+  {
+    const int m = 128 * wm + lrow;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      a_addr[kk] = smem_addr + m * 64 + (((2 * kk + lq) ^ swz4(m)) * 16);
+    const int tr_row = (lane & 15) >> 2;
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = bcol[j] + tr_col;
+      const int r0 = 8 * lq + tr_row;  // r0 & 3 == tr_row
+      b_addr[j] = smem_addr + A_STAGE2 + r0 * 512 + ((col >> 3) ^ (4 * tr_row)) * 16 + (col & 7) * 2;
+    }
   }
-  // the last nk % 4 steps (only when K is not a multiple of 128)
-  for (; kt < nk; ++kt) {
-    const int st = kt & 3;
-    MOE_STEP(st);
+
+  // Fragment registers, two sets: while the MFMAs of one half-step read one
+  // set, the LDS reads of the next half-step fill the other. Each read and
+  // its MFMAs sit in one asm block that ends by waiting for the reads, so no
+  // load is ever in flight outside the block that issued it (the transposing
+  // read is written in asm because the compiler cannot tell it apart from
+  // the LDS writes of the copies still in flight). Each block starts with a
+  // few wait states so that a register the compiler wrote just before (the
+  // zeroed accumulators, a fragment half it had to move) is settled before
+  // an MFMA reads it.
+  bf16x8_t xa0, xa1, xa2, xa3, xb0, xb1;
+  bf16x8_t ya0, ya1, ya2, ya3, yb0, yb1;
+  s16x4_t h0, h1, h2, h3;
+#define MOE_JOIN_B(B0, B1)                                                           \
+  do {                                                                               \
+    const s16x8_t v0 = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};    \
+    const s16x8_t v1 = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};    \
+    B0 = __builtin_bit_cast(bf16x8_t, v0);                                          \
+    B1 = __builtin_bit_cast(bf16x8_t, v1);                                          \
+  } while (0)
+#define MOE_MF_4                                                                    \
+  "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c20], %[a2], %[b0], %[c20]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c21], %[a2], %[b1], %[c21]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c30], %[a3], %[b0], %[c30]\n\t"                       \
+  "v_mfma_f32_32x32x16_bf16 %[c31], %[a3], %[b1], %[c31]\n\t"
+#define MOE_READS(OFF0, OFF1)                                                       \
+  "ds_read_b128 %[na0], %[aa]\n\t"                                                  \
+  "ds_read_b128 %[na1], %[aa] offset:2048\n\t"                                      \
+  "ds_read_b128 %[na2], %[aa] offset:4096\n\t"                                      \
+  "ds_read_b128 %[na3], %[aa] offset:6144\n\t"                                      \
+  "ds_read_b64_tr_b16 %[h0], %[ba0] offset:" OFF0 "\n\t"                            \
+  "ds_read_b64_tr_b16 %[h1], %[ba0] offset:" OFF1 "\n\t"                            \
+  "ds_read_b64_tr_b16 %[h2], %[ba1] offset:" OFF0 "\n\t"                            \
+  "ds_read_b64_tr_b16 %[h3], %[ba1] offset:" OFF1 "\n\t"
+#define MOE_ACC_OUT                                                                 \
+  [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]),              \
+      [c11] "+v"(acc[1][1]), [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]),          \
+      [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1])
+  // reads of a half-step into set N (A at AA, B at BA0/BA1 + OFF0/OFF1) while
+  // the MFMAs (string MF) consume set C
+#define MOE_RM_ASM(OFF0, OFF1, AA, BA0, BA1, N, C, MF)                              \
+  asm volatile("s_nop 4\n\t" MOE_READS(OFF0, OFF1) MF "s_waitcnt lgkmcnt(0)"       \
+               : [na0] "=&v"(N##a0), [na1] "=&v"(N##a1), [na2] "=&v"(N##a2),         \
+                 [na3] "=&v"(N##a3), [h0] "=&v"(h0), [h1] "=&v"(h1),                 \
+                 [h2] "=&v"(h2), [h3] "=&v"(h3), MOE_ACC_OUT                        \
+               : [a0] "v"(C##a0), [a1] "v"(C##a1), [a2] "v"(C##a2),                  \
+                 [a3] "v"(C##a3), [b0] "v"(C##b0), [b1] "v"(C##b1),                  \
+                 [aa] "v"(AA), [ba0] "v"(BA0), [ba1] "v"(BA1)                        \
+               : "memory")
+#define MOE_READ_MMA(OFF0, OFF1, AA, BA0, BA1, N, C)                                \
+  do {                                                                              \
+    MOE_RM_ASM(OFF0, OFF1, AA, BA0, BA1, N, C, MOE_MF_4);                           \
+    MOE_JOIN_B(N##b0, N##b1);                                                       \
+  } while (0)
+  // MFMAs only, on set y (the last half-step)
+#define MOE_MMA_ASM(MF)                                                             \
+  asm volatile("s_nop 4\n\t" MF                                                   \
+               : MOE_ACC_OUT                                                        \
+               : [a0] "v"(ya0), [a1] "v"(ya1), [a2] "v"(ya2), [a3] "v"(ya3),         \
+                 [b0] "v"(yb0), [b1] "v"(yb1))
+
+  // A wave whose 128 rows all lie past the segment end (the segment tail
+  // of an expert often fills less than half of its last tile) skips its
+  // LDS reads and MFMAs and only keeps the copies and barriers going.
+  const bool idle = __builtin_amdgcn_readfirstlane(row_end - row0 <= 128 * wm) != 0;
+
+  // copies of the first NSTAGE_DMA steps in flight, then wait for step 0's
+#pragma unroll
+  for (int s = 0; s < NSTAGE_DMA; ++s)
+    if (s < nk) issue(s, s * STAGE2);
+  {
+    const int ahead = min(NSTAGE_DMA - 1, nk - 1);  // copy groups that may still fly
+    if (ahead >= 4) wait_vmcnt<4 * PER>();
+    else if (ahead == 3) wait_vmcnt<3 * PER>();
+    else if (ahead == 2) wait_vmcnt<2 * PER>();
+    else if (ahead == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
-#undef MOE_STEP
+  if (idle) {
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const int ahead = min(NSTAGE_DMA - 2, nk - 2 - kt);
+      if (ahead >= 3) wait_vmcnt<3 * PER>();
+      else if (ahead == 2) wait_vmcnt<2 * PER>();
+      else if (ahead == 1) wait_vmcnt<PER>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NSTAGE_DMA < nk) issue(kt + NSTAGE_DMA, (uint32_t)(kt % NSTAGE_DMA) * STAGE2);
+    }
+  } else {
+    // fragments of half-step (0, 0) -> set x
+    asm volatile(MOE_READS("0", "2048") "s_waitcnt lgkmcnt(0)"
+                 : [na0] "=&v"(xa0), [na1] "=&v"(xa1), [na2] "=&v"(xa2), [na3] "=&v"(xa3),
+                   [h0] "=&v"(h0), [h1] "=&v"(h1), [h2] "=&v"(h2), [h3] "=&v"(h3)
+                 : [aa] "v"(a_addr[0]), [ba0] "v"(b_addr[0]), [ba1] "v"(b_addr[1])
+                 : "memory");
+    MOE_JOIN_B(xb0, xb1);
+
+    // Step kt: (kt, 1) is read into set y while (kt, 0) multiplies set x;
+    // then the copies of step kt+1 are waited for and the barrier certifies
+    // them (and that every wave is done reading stage kt, which the copies of
+    // step kt+NSTAGE_DMA then overwrite); then (kt+1, 0) is read into set x while
+    // (kt, 1) multiplies set y.
+    int kt = 0;
+    uint32_t so = 0;  // byte offset of stage kt % NSTAGE_DMA
+    for (; kt + 1 < nk; ++kt) {
+      const uint32_t so1 = so + STAGE2 == NSTAGE_DMA * STAGE2 ? 0u : so + STAGE2;
+      MOE_READ_MMA("8192", "10240", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, y, x);
+      const int ahead = min(NSTAGE_DMA - 2, nk - 2 - kt);
+      if (ahead >= 3) wait_vmcnt<3 * PER>();
+      else if (ahead == 2) wait_vmcnt<2 * PER>();
+      else if (ahead == 1) wait_vmcnt<PER>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NSTAGE_DMA < nk) issue_a(kt + NSTAGE_DMA, so);
+      MOE_READ_MMA("0", "2048", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1, x, y);
+      if (kt + NSTAGE_DMA < nk) issue_b(kt + NSTAGE_DMA, so);
+      so = so1;
+    }
+    {
+      // last step: (kt, 1) into set y while (kt, 0) multiplies, then (kt, 1)
+      MOE_READ_MMA("8192", "10240", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, y, x);
+      MOE_MMA_ASM(MOE_MF_4);
+    }
+  }
+  // the last MFMAs finish writing the accumulators before any VALU reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#undef MOE_MMA_ASM
+#undef MOE_READ_MMA
+#undef MOE_RM_ASM
+#undef MOE_ACC_OUT
+#undef MOE_READS
+#undef MOE_MF_4
+#undef MOE_JOIN_B
+
+  // ---- split tiles: partial sums through the workspace. A slot holds the
+  // 256 x 256 accumulators in register order, 16 bytes per lane per store:
+  // float4 (wave, q, lane) with q = 4 (2i + j) + r/4 holds acc[i][j][r..r+3].
+  if (S > 1) {
+    float4* mine = reinterpret_cast<float4*>(a.split_ws) + wave * 32 * 64 + lane;
+    if (part < S - 1) {
+      float4* dst = mine + (size_t)(slot0 + part) * (BM2 * BN2 / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            dst[((2 * i + j) * 4 + rq) * 64] =
+                make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                            acc[i][j][4 * rq + 3]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();  // every wave's partial sums are in memory
+      if (tid == 0) {
+        __hip_atomic_store(a.split_flags + slot0 + part, 1, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+    for (int p = 0; p < S - 1; ++p) {
+      if (tid == 0) {
+        // bounded wait: the part was dispatched before this workgroup and
+        // never waits itself, so the flag rises within its run time
+        for (int spin = 0; spin < (1 << 24); ++spin) {
+          if (__hip_atomic_load(a.split_flags + slot0 + p, __ATOMIC_ACQUIRE,
+                                __HIP_MEMORY_SCOPE_AGENT) != 0)
+            break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        __hip_atomic_store(a.split_flags + slot0 + p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      const float4* src = mine + (size_t)(slot0 + p) * (BM2 * BN2 / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const float4 v = src[((2 * i + j) * 4 + rq) * 64];
+            acc[i][j][4 * rq] += v.x;
+            acc[i][j][4 * rq + 1] += v.y;
+            acc[i][j][4 * rq + 2] += v.z;
+            acc[i][j][4 * rq + 3] += v.w;
+          }
+    }
+  }
 
   // ---- epilogue through LDS, so that global stores are 16 bytes per lane.
   // Accumulator r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of
@@ -734,6 +914,8 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
     a.n_tiles_n = mode == MODE_SWIGLU ? ceil_div(p.N, 128) : ceil_div(p.N, 256);
   const long long total = (long long)a.max_tiles * a.n_tiles_n;
   a.per_xcd = ceil_div(total, 8);
+  a.split_ws = p.split_ws;
+  a.split_flags = p.split_flags;
   a.B0 = p.B0;
   a.B1 = p.B1;
   a.S0 = p.S0;
@@ -741,12 +923,14 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   a.clamp = p.clamp;
   a.out = p.out;
   const dim3 grid(8 * a.per_xcd);
+  // bf16: an XCD's share of the tiles plus the split parts of its last round
+  const dim3 grid_bf16(8 * (a.per_xcd + kCUsPerXCD));
   if (mode == MODE_SWIGLU) {
     if (p.mxfp4) gemm_kernel<MODE_SWIGLU, true><<<grid, 256, 0, s>>>(a);
-    else gemm_bf16_kernel<MODE_SWIGLU><<<grid, 512, 0, s>>>(a);
+    else gemm_bf16_kernel<MODE_SWIGLU><<<grid_bf16, 512, 0, s>>>(a);
   } else {
     if (p.mxfp4) gemm_kernel<MODE_DOWN, true><<<grid, 256, 0, s>>>(a);
-    else gemm_bf16_kernel<MODE_DOWN><<<grid, 512, 0, s>>>(a);
+    else gemm_bf16_kernel<MODE_DOWN><<<grid_bf16, 512, 0, s>>>(a);
   }
   return hipGetLastError();
 }

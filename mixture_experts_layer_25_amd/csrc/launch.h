@@ -28,6 +28,18 @@ inline int max_mtiles(const moe_cfg& c) {
 }
 // int32 entries of the tile map: [0] = tile count, then (expert, row0) pairs.
 inline size_t tilemap_ints(const moe_cfg& c) { return 1 + 2 * (size_t)max_mtiles(c); }
+// bf16 grouped GEMMs split the tiles of their last round along K: one slot
+// of 256 x 256 fp32 partial sums per split part (at most 32 per XCD), and
+// one ready flag per slot.
+constexpr int kSplitSlots = 256;
+constexpr size_t kSplitSlotBytes = 256 * 256 * 4;
+constexpr size_t kSplitFlagBytes = 1024;
+inline bool gemm_splits(const moe_cfg& c) {
+  return c.act_dtype == MOE_BF16 && c.w_dtype == MOE_BF16;
+}
+inline size_t split_bytes(const moe_cfg& c) {
+  return gemm_splits(c) ? kSplitFlagBytes + kSplitSlots * kSplitSlotBytes : 0;
+}
 inline int num_chunks(const moe_cfg& c) { return ceil_div(c.T, kChunk); }
 
 hipError_t launch_router(const moe_cfg& c, const void* x, const float* W_r, const float* bias,
@@ -40,7 +52,9 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
 
 // Builds the tile map (tilemap_ints(c) int32, M-tiles of gemm_bm(c) rows)
 // from device offsets.
-hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap, hipStream_t s);
+// also zeroes the kSplitSlots split flags when `flags` is not null.
+hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
+                          int32_t* flags, hipStream_t s);
 
 // bf16 activations: grouped MFMA GEMMs over the tile map. A dense launch
 // (tilemap == nullptr) treats rows [0, rows) as one segment of expert 0.
@@ -59,6 +73,8 @@ struct GemmProblem {
   int mxfp4;
   float clamp;
   void* out;               // SwiGLU: H bf16 [rows][N]; down: fp32 [rows][N]
+  float* split_ws;         // kSplitSlots partial-sum slots, or nullptr: no split
+  int32_t* split_flags;    // kSplitSlots flags, zero before the launch
 };
 hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);
