@@ -7,21 +7,28 @@
 // clamped to [-L, L] before SiLU(gate)*up; routed experts may be FP4
 // (here MXFP4: e2m1 codes with an e8m0 scale per 32 K-elements).
 //
-// Tile: 128 rows x 512 B-columns x 32 K per stage, 256 threads (4 waves).
+// Two kernels share the operand formats below.
+//
+// MXFP4 weights (gemm_kernel<MODE, true>): tile 128 rows x 512 B-columns x
+// 32 k per stage, 256 threads (4 waves, 128 x 128 each, 256 accumulators).
 //   SwiGLU: the 512 B-columns are 256 gate and the same 256 up columns, so
 //   each wave's accumulators hold gate and up of the same (row, f) and the
 //   epilogue forms h = SiLU(clamp(g)) * clamp(u) in registers and stores
 //   bf16 H; the gate/up intermediate never reaches memory.
 //   Down: 512 output columns, fp32 stores.
-// Each wave computes 128 rows x 128 B-columns with v_mfma_f32_32x32x16_bf16
-// (4 x 4 tiles, 256 fp32 accumulators per lane).
+//   Two LDS stages and three register sets: during step kt the MFMAs read
+//   LDS stage kt%2, the registers holding step kt+1 are stored to the other
+//   stage, and the global loads of steps kt+2 and kt+3 are in flight.
+// bf16 weights (gemm_bf16_kernel<MODE>): 256 x 256 tiles, 8 waves,
+//   asynchronous global->LDS copies five stages deep (described at the
+//   kernel).
 //
-// Operands reach MFMA K-contiguous: a lane's fragment is 8 consecutive k of
-// one row (A) or one column (B).
+// Operands reach MFMA (v_mfma_f32_32x32x16_bf16) K-contiguous: a lane's
+// fragment is 8 consecutive k of one row (A) or one column (B).
 //   A (X rows, K-contiguous): 16-byte loads, stored as [row][4 k-groups] and
 //   read with ds_read_b128.
-//   B bf16 ([K][N], N-contiguous): whole 1 KB k-rows are stored untouched;
-//   the MFMA fragment is read with the gfx950 transposing LDS load
+//   B bf16 ([K][N], N-contiguous): whole k-rows are stored untouched; the
+//   MFMA fragment is read with the gfx950 transposing LDS load
 //   ds_read_b64_tr_b16 (within a 16-lane group, lane i receives element i of
 //   the 4 rows the group points at), two per fragment, so no transpose runs
 //   on the vector ALUs.
@@ -34,13 +41,8 @@
 // stores and on the MFMA fragment reads (checked with the LDS bank-conflict
 // counter).
 //
-// Pipeline: two LDS stages and three register sets. During step kt the MFMAs
-// read LDS stage kt%2, the registers holding step kt+1 are stored to the
-// other stage, and the global loads of steps kt+2 and kt+3 are in flight.
-// One barrier per 32-k step.
-//
-// Workgroup -> tile: workgroup b runs on XCD (b mod 8), and b is remapped so
-// that each XCD takes a contiguous range of the tile order (tile_of), whose
+// Workgroup -> tile: workgroup b runs on XCD (b mod 8), and each XCD walks a
+// contiguous range of the tile order (tile_of, expert_tile_of), whose
 // neighbours share weight and activation slabs in that XCD's L2.
 #include "common.h"
 #include "launch.h"
@@ -158,6 +160,33 @@ __device__ __forceinline__ void tile_of(int L, int MT, int NT, int& mt, int& nt)
   const int gs = min(G, NT - g * G);
   mt = rem / gs;
   nt = g * G + rem % gs;
+}
+
+// Tile order of the bf16 kernel, by expert: an expert's tiles are
+// contiguous, in groups of up to 8 of its M-tiles; inside a group N-tile
+// major and M-tile minor. The 32 workgroups an XCD runs at once then cover
+// about 8 M-tiles x 4 N-tiles of one expert, so each weight slab is fetched
+// once and shared by all those M-tiles, and each activation slab by 4
+// N-tiles. With a tile map, the M-tiles t / NT and the tile's own belong
+// to the same expert (an expert's tiles span whole rows of NT), which
+// gives the expert's first M-tile and count without a search.
+__device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int32_t* tilemap,
+                                               const int32_t* offsets, int bm, int& mt, int& nt) {
+  constexpr int MG = 8;
+  int first = 0, m = MT;
+  if (tilemap) {
+    const int g = t / NT;
+    const int e = tilemap[1 + 2 * g];
+    const int seg = offsets[e];
+    first = g - (tilemap[2 + 2 * g] - seg) / bm;
+    m = (offsets[e + 1] - seg + bm - 1) / bm;
+  }
+  const int r = t - first * NT;
+  const int gi = r / (MG * NT);
+  const int gsz = min(MG, m - gi * MG);
+  const int rr = r - gi * MG * NT;
+  nt = rr / gsz;
+  mt = first + gi * MG + rr % gsz;
 }
 
 template <int MODE, bool MX>
@@ -506,7 +535,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
 
   // ---- workgroup -> (tile, k-range). Workgroup b runs on XCD x = b mod 8
   // as that XCD's i-th workgroup. The real tiles (M-tiles from the tile map
-  // x N-tiles, in tile_of order) are cut into 8 contiguous ranges, one per
+  // x N-tiles, in expert_tile_of order) are cut into 8 contiguous ranges, one per
   // XCD. An XCD's whole rounds of kCUsPerXCD tiles run as whole tiles; the
   // tiles of its last, partial round are each split along K into S parts
   // (S x remainder <= kCUsPerXCD) so that the last round keeps every CU busy.
@@ -535,7 +564,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
     slot0 = xcd * kCUsPerXCD + (u / S) * (S - 1);
   }
   int mt, nt;
-  tile_of(tile, MT, a.n_tiles_n, mt, nt);
+  expert_tile_of(tile, MT, a.n_tiles_n, a.tilemap, a.offsets, BM2, mt, nt);
   int e, row0, row_end;
   if (a.tilemap) {
     e = a.tilemap[1 + 2 * mt];
