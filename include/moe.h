@@ -114,9 +114,13 @@ typedef struct moe_weights {
 } moe_weights;
 
 /* Bytes of workspace a call needs (host out-parameter `bytes`).
- * MOE_WS_DISPATCH for moe_dispatch, MOE_WS_EXPERT_FFN for moe_expert_ffn,
- * MOE_WS_FORWARD for moe_forward (holds x_perm, H, y_perm and, with a
- * shared expert, its H and output). */
+ * MOE_WS_DISPATCH for moe_dispatch (per-chunk expert counts),
+ * MOE_WS_EXPERT_FFN for moe_expert_ffn / _gate_up / _down (the device tile
+ * map and, with bf16 weights, 64 MiB of fp32 partial sums plus ready flags
+ * for the GEMM tiles that are split along K), MOE_WS_FORWARD for
+ * moe_forward (all of the above plus x_perm, H, y_perm and, with a shared
+ * expert, its H and output). A workspace carries state only within one
+ * call; calls that run concurrently need separate workspaces. */
 int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes);
 
 /* Router ("FFN, SwiGLU and MoE" sec. 3; "ops-transformer" MoEForward steps

@@ -1,0 +1,99 @@
+"""Check of the grouped-GEMM assembly for MFMA result hazards.
+
+The GEMM inner loops are inline-asm blocks that end with MFMAs. The compiler
+does not look inside inline asm, so if it places an instruction that reads
+or overwrites an MFMA destination register right after such a block (a
+register move, a spill), nothing guarantees the wait states the hardware
+needs, and the value read can be stale. This module compiles a HIP source
+to gfx950 assembly and reports every compiler instruction, within the first
+few after an MFMA-terminated asm block, that touches a register one of the
+block's trailing MFMAs writes.
+
+    python -m mixture_experts_layer_25_amd.asmcheck [source.hip]
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+WINDOW = 6  # instructions checked after each block
+
+
+def _regs(op: str) -> set:
+    m = re.match(r"([av])\[(\d+):(\d+)\]$", op)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([av])(\d+)$", op)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def find_hazards(asm: str) -> list[str]:
+    lines = asm.split("\n")
+    found = []
+    func = "?"
+    i = 0
+    while i < len(lines):
+        line = lines[i]
+        if re.match(r"^_Z\S+:", line):
+            func = line.split(":")[0]
+        if ";;#ASMSTART" in line:
+            j = i + 1
+            body = []
+            while j < len(lines) and ";;#ASMEND" not in lines[j]:
+                t = lines[j].strip()
+                if t and not t.startswith(";"):
+                    body.append(t)
+                j += 1
+            dst = set()
+            for t in reversed(body):
+                if t.startswith("s_waitcnt"):
+                    continue
+                if not t.startswith("v_mfma"):
+                    break
+                dst |= _regs(t.split()[1].rstrip(","))
+            if dst:
+                k, n = j + 1, 0
+                while n < WINDOW and k < len(lines) and ";;#ASMSTART" not in lines[k]:
+                    t = lines[k].strip()
+                    if t and not t.startswith((";", ".")):
+                        touched = set()
+                        for op in re.findall(r"[av]\[\d+:\d+\]|\b[av]\d+\b", t):
+                            touched |= _regs(op)
+                        if touched & dst:
+                            found.append(f"{func}: {t}")
+                        n += 1
+                    k += 1
+            i = j
+        i += 1
+    return found
+
+
+def compile_to_asm(src: str) -> str:
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang",
+                        "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only",
+                        "-S", src, "-o", out], check=True, capture_output=True,
+                       cwd=os.path.dirname(src))
+        return open(out).read()
+
+
+def main(argv=None) -> int:
+    argv = sys.argv[1:] if argv is None else argv
+    src = argv[0] if argv else os.path.join(HERE, "csrc", "gemm.hip")
+    hazards = find_hazards(compile_to_asm(src))
+    for h in hazards:
+        print(h)
+    print(f"{len(hazards)} MFMA result hazards after asm blocks in {os.path.basename(src)}")
+    return 1 if hazards else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

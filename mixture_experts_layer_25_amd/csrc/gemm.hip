@@ -508,6 +508,10 @@ constexpr int B_STAGE2 = BN2 * BK * 2;   // 16 KB
 constexpr int STAGE2 = A_STAGE2 + B_STAGE2;
 constexpr int kCUsPerXCD = 32;      // MI355X: 256 CUs in 8 XCDs
 constexpr int kMaxSplit = 8;        // K-parts of a split tile
+// Wait states after an asm block's last MFMA so that whatever the compiler
+// places next (a register move, a spill, a VALU read) sees the finished
+// accumulator: the compiler does not look inside asm for MFMA hazards.
+#define MFMA_TAIL "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
 constexpr int NSTAGE_DMA = 5;       // 5 x 32 KB = 160 KB, all of the LDS
 static_assert(NSTAGE_DMA >= 2 && NSTAGE_DMA <= 5, "copy waits are written for 2..5 stages");
 
@@ -523,6 +527,58 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// ---- bf16 kernels: workgroup -> (tile, k-range). Workgroup b runs on XCD
+// x = b mod 8 as that XCD's i-th workgroup. The real tiles (M-tiles from
+// the tile map x N-tiles, in expert_tile_of order) are cut into 8
+// contiguous ranges, one per XCD. An XCD's whole rounds of kCUsPerXCD
+// tiles run as whole tiles; the tiles of its last, partial round are each
+// split along K into S parts (S x remainder <= kCUsPerXCD) so that the
+// last round keeps every CU busy. Parts 0..S-2 leave fp32 partial sums in
+// a workspace slot and raise its flag; part S-1 (the highest workgroup
+// index of the tile, so the parts it waits for were dispatched before it)
+// adds them in part order and runs the epilogue.
+struct Job {
+  int e, row0, row_end, nt, S, part, slot0, kt_begin, nk;
+};
+__device__ __forceinline__ bool schedule_bf16(const Args& a, int b, Job& j) {
+  const int xcd = b & 7, wi = b >> 3;
+  const int MT = a.tilemap ? a.tilemap[0] : a.max_tiles;
+  const int total = MT * a.n_tiles_n;
+  const int t_lo = (int)((long long)total * xcd / 8);
+  const int t_hi = (int)((long long)total * (xcd + 1) / 8);
+  const int whole = (t_hi - t_lo) / kCUsPerXCD * kCUsPerXCD;
+  const int rem = t_hi - t_lo - whole;
+  const int nk_all = a.K / BK;
+  int tile;
+  j.S = 1;
+  j.part = 0;
+  j.slot0 = 0;
+  if (wi < whole) {
+    tile = t_lo + wi;
+  } else {
+    if (a.split_flags && rem > 0) j.S = min(min(kMaxSplit, kCUsPerXCD / rem), nk_all);
+    const int u = wi - whole;
+    if (u >= rem * j.S) return false;
+    tile = t_lo + whole + u / j.S;
+    j.part = u % j.S;
+    j.slot0 = xcd * kCUsPerXCD + (u / j.S) * (j.S - 1);
+  }
+  int mt;
+  expert_tile_of(tile, MT, a.n_tiles_n, a.tilemap, a.offsets, kBM_BF16, mt, j.nt);
+  if (a.tilemap) {
+    j.e = a.tilemap[1 + 2 * mt];
+    j.row0 = a.tilemap[2 + 2 * mt];
+    j.row_end = a.offsets[j.e + 1];
+  } else {
+    j.e = 0;
+    j.row0 = mt * kBM_BF16;
+    j.row_end = a.rows;
+  }
+  j.kt_begin = j.part * nk_all / j.S;
+  j.nk = (j.part + 1) * nk_all / j.S - j.kt_begin;
+  return true;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[NSTAGE_DMA * STAGE2];
@@ -533,50 +589,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
   const int wm = wave >> 2;   // row half
   const int wn = wave & 3;    // column quarter
 
-  // ---- workgroup -> (tile, k-range). Workgroup b runs on XCD x = b mod 8
-  // as that XCD's i-th workgroup. The real tiles (M-tiles from the tile map
-  // x N-tiles, in expert_tile_of order) are cut into 8 contiguous ranges, one per
-  // XCD. An XCD's whole rounds of kCUsPerXCD tiles run as whole tiles; the
-  // tiles of its last, partial round are each split along K into S parts
-  // (S x remainder <= kCUsPerXCD) so that the last round keeps every CU busy.
-  // Parts 0..S-2 leave fp32 partial sums in a workspace slot and raise its
-  // flag; part S-1 (the highest workgroup index of the tile, so the parts it
-  // waits for were dispatched before it) adds them in part order and runs
-  // the epilogue.
-  const int b = blockIdx.x;
-  const int xcd = b & 7, wi = b >> 3;
-  const int MT = a.tilemap ? a.tilemap[0] : a.max_tiles;
-  const int total = MT * a.n_tiles_n;
-  const int t_lo = (int)((long long)total * xcd / 8);
-  const int t_hi = (int)((long long)total * (xcd + 1) / 8);
-  const int whole = (t_hi - t_lo) / kCUsPerXCD * kCUsPerXCD;
-  const int rem = t_hi - t_lo - whole;
-  const int nk_all = a.K / BK;
-  int tile, S = 1, part = 0, slot0 = 0;
-  if (wi < whole) {
-    tile = t_lo + wi;
-  } else {
-    if (a.split_flags && rem > 0) S = min(min(kMaxSplit, kCUsPerXCD / rem), nk_all);
-    const int u = wi - whole;
-    if (u >= rem * S) return;
-    tile = t_lo + whole + u / S;
-    part = u % S;
-    slot0 = xcd * kCUsPerXCD + (u / S) * (S - 1);
-  }
-  int mt, nt;
-  expert_tile_of(tile, MT, a.n_tiles_n, a.tilemap, a.offsets, BM2, mt, nt);
-  int e, row0, row_end;
-  if (a.tilemap) {
-    e = a.tilemap[1 + 2 * mt];
-    row0 = a.tilemap[2 + 2 * mt];
-    row_end = a.offsets[e + 1];
-  } else {
-    e = 0;
-    row0 = mt * BM2;
-    row_end = a.rows;
-  }
-  const int kt_begin = part * nk_all / S;
-  const int nk = (part + 1) * nk_all / S - kt_begin;
+  Job jb;
+  if (!schedule_bf16(a, blockIdx.x, jb)) return;
+  const int e = jb.e, row0 = jb.row0, row_end = jb.row_end, nt = jb.nt;
+  const int S = jb.S, part = jb.part, slot0 = jb.slot0, kt_begin = jb.kt_begin, nk = jb.nk;
   const int K = a.K, N = a.N;
   const int n0 = MODE == MODE_SWIGLU ? nt * 128 : nt * 256;
 
@@ -801,9 +817,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Args a) {
       so = so1;
     }
     {
-      // last step: (kt, 1) into set y while (kt, 0) multiplies, then (kt, 1)
-      MOE_READ_MMA("8192", "10240", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, y, x);
-      MOE_MMA_ASM(MOE_MF_4);
+      // last step: (kt, 1) into set y while (kt, 0) multiplies, then (kt, 1);
+      // both blocks end with the MFMA result wait states (the compiler may
+      // move accumulators after them)
+      MOE_RM_ASM("8192", "10240", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, y, x,
+                 MOE_MF_4 MFMA_TAIL);
+      MOE_JOIN_B(yb0, yb1);
+      MOE_MMA_ASM(MOE_MF_4 MFMA_TAIL);
     }
   }
   // the last MFMAs finish writing the accumulators before any VALU reads them
