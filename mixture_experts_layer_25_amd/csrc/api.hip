@@ -198,7 +198,7 @@ hipError_t run_shared(const moe_cfg& c, const void* x, const moe_weights& w, voi
   g.tilemap = nullptr;
   g.offsets = nullptr;
   g.rows = c.T;
-  g.max_tiles = moe::ceil_div(c.T, moe::kBM_BF16);  // shared expert: bf16 weights
+  g.max_tiles = moe::ceil_div(c.T, moe::kBM);
   g.E = 1;
   g.mxfp4 = 0;
   g.clamp = c.clamp;

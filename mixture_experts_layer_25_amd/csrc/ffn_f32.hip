@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restri
 
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
                           int32_t* flags, hipStream_t s) {
-  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, gemm_bm(c), tilemap, flags);
+  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, kBM, tilemap, flags);
   return hipGetLastError();
 }
 

@@ -10,10 +10,9 @@
 
 namespace moe {
 
-// Rows per M-tile of the grouped GEMMs (both projections): 256 for bf16
-// weights, 128 for MXFP4 weights.
-constexpr int kBM = 128;
-constexpr int kBM_BF16 = 256;
+// Rows per M-tile of the grouped GEMMs (both projections, bf16 and MXFP4
+// weights).
+constexpr int kBM = 256;
 // Tokens per dispatch chunk (one workgroup of the count and rank kernels).
 constexpr int kChunk = 256;
 
@@ -22,21 +21,16 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Upper bound of the number of M-tiles: every kept row in a full tile plus
 // one partial tile per expert.
-inline int gemm_bm(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? kBM_BF16 : kBM; }
-inline int max_mtiles(const moe_cfg& c) {
-  return ceil_div((long long)c.T * c.top_k, gemm_bm(c)) + c.E;
-}
+inline int max_mtiles(const moe_cfg& c) { return ceil_div((long long)c.T * c.top_k, kBM) + c.E; }
 // int32 entries of the tile map: [0] = tile count, then (expert, row0) pairs.
 inline size_t tilemap_ints(const moe_cfg& c) { return 1 + 2 * (size_t)max_mtiles(c); }
-// bf16 grouped GEMMs split the tiles of their last round along K: one slot
+// The grouped GEMMs split the tiles of their last round along K: one slot
 // of 256 x 256 fp32 partial sums per split part (at most 32 per XCD), and
 // one ready flag per slot.
 constexpr int kSplitSlots = 256;
 constexpr size_t kSplitSlotBytes = 256 * 256 * 4;
 constexpr size_t kSplitFlagBytes = 1024;
-inline bool gemm_splits(const moe_cfg& c) {
-  return c.act_dtype == MOE_BF16 && c.w_dtype == MOE_BF16;
-}
+inline bool gemm_splits(const moe_cfg& c) { return c.act_dtype == MOE_BF16; }
 inline size_t split_bytes(const moe_cfg& c) {
   return gemm_splits(c) ? kSplitFlagBytes + kSplitSlots * kSplitSlotBytes : 0;
 }
@@ -50,7 +44,7 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
                            int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,
                            int32_t* chunk_ws, hipStream_t s);
 
-// Builds the tile map (tilemap_ints(c) int32, M-tiles of gemm_bm(c) rows)
+// Builds the tile map (tilemap_ints(c) int32, M-tiles of kBM rows)
 // from device offsets.
 // also zeroes the kSplitSlots split flags when `flags` is not null.
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
