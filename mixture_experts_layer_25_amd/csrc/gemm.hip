@@ -42,10 +42,11 @@
 // register staging) into a ring of stages (5 x 32 KB for bf16, 7 x 21 KB
 // for MXFP4). Each 32-k step is two half-steps of 16 k; the MFMA fragments
 // of a half-step are read from LDS while the MFMAs of the previous
-// half-step run (two register sets). In the middle of step kt one barrier
-// certifies the copies of step kt+1 and that every wave is done reading
-// stage kt, whose copies for step kt+NSTAGE are then issued, in two halves
-// around the next half-step's MFMAs.
+// half-step run (two register sets). One barrier per two steps, in the
+// middle of every odd step kt, certifies the copies of steps kt+1 and kt+2
+// and that every wave is done reading the stages of steps up to kt; each
+// step issues the copies of step kt - 1 + NSTAGE (into the stage of step
+// kt - 1), in two halves around a half-step's MFMAs.
 //
 // Tile schedule (schedule_tile): the real tiles, in expert_tile_of order,
 // are cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD
@@ -74,6 +75,7 @@ struct Stages {
   static constexpr int bytes = MX ? A_BYTES + MXC_BYTES + MXS_BYTES : A_BYTES + B_BYTES;
   static constexpr int count = MX ? 7 : 5;  // 147 KB / 160 KB of the 160 KB LDS
   static constexpr int per = MX ? 3 : 4;    // copies per thread per step
+  static_assert(count >= 4, "a barrier every two steps needs four stages");
 };
 
 enum { MODE_SWIGLU = 0, MODE_DOWN = 1 };
@@ -487,27 +489,31 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   // LDS reads and MFMAs and only keeps the copies and barriers going.
   const bool idle = __builtin_amdgcn_readfirstlane(row_end - row0 <= 128 * wm) != 0;
 
-  // copies of the first NST steps in flight, then wait for step 0's
+  // copies of the first NST - 1 steps in flight, then wait for steps 0 and 1
 #pragma unroll
-  for (int s = 0; s < NST; ++s)
+  for (int s = 0; s < NST - 1; ++s)
     if (s < nk) {
       issue_a(s, s * SB);
       issue_b(s, s * SB);
     }
-  wait_copy_groups<PER>(min(NST - 1, nk - 1));
+  wait_copy_groups<PER>(min(NST - 2, nk - 1) - min(1, nk - 1));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
   if (idle) {
+    uint32_t si = (uint32_t)(NST - 1) * SB;
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      wait_copy_groups<PER>(min(NST - 2, nk - 2 - kt));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (kt + NST < nk) {
-        const uint32_t so = (uint32_t)(kt % NST) * SB;
-        issue_a(kt + NST, so);
-        issue_b(kt + NST, so);
+      const int is = kt - 1 + NST;  // step whose copies this iteration issues
+      if (kt & 1) {
+        wait_copy_groups<PER>(min(nk - 1, kt - 2 + NST) - min(kt + 2, nk - 1));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
+      if (is < nk) {
+        issue_a(is, si);
+        issue_b(is, si);
+      }
+      si = si + SB == NST * SB ? 0u : si + SB;
     }
   } else {
     // fragments of half-step (0, 0) -> set x
@@ -533,24 +539,30 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     }
 
     // Step kt: (kt, 1) is read into set y while (kt, 0) multiplies set x;
-    // then the copies of step kt+1 are waited for and the barrier certifies
-    // them (and that every wave is done reading stage kt, which the copies
-    // of step kt+NST then overwrite); then (kt+1, 0) is read into set x
-    // while (kt, 1) multiplies set y.
+    // after odd steps the barrier certifies the copies of steps kt+1 and
+    // kt+2; then (kt+1, 0) is read into set x while (kt, 1) multiplies set
+    // y. The copies of step kt - 1 + NST go to the stage of step kt - 1,
+    // which every wave finished reading before the last barrier.
     int kt = 0;
-    uint32_t so = 0;  // byte offset of stage kt % NST
+    uint32_t so = 0;                         // byte offset of stage kt % NST
+    uint32_t si = (uint32_t)(NST - 1) * SB;  // stage of step kt - 1 + NST
     for (; kt + 1 < nk; ++kt) {
       const uint32_t so1 = so + SB == NST * SB ? 0u : so + SB;
+      const int is = kt - 1 + NST;  // step whose copies this iteration issues
       G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
               s_addr[0] + so, s_addr[1] + so, y, x, G_MF);
-      wait_copy_groups<PER>(min(NST - 2, nk - 2 - kt));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (kt + NST < nk) issue_a(kt + NST, so);
+      if (kt & 1) {
+        // certify steps kt+1 and kt+2; every wave is done with steps < kt+1
+        wait_copy_groups<PER>(min(nk - 1, kt - 2 + NST) - min(kt + 2, nk - 1));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      if (is < nk) issue_a(is, si);
       G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
               s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF);
-      if (kt + NST < nk) issue_b(kt + NST, so);
+      if (is < nk) issue_b(is, si);
       so = so1;
+      si = si + SB == NST * SB ? 0u : si + SB;
     }
     // last step; these blocks end with the MFMA result wait states since
     // the compiler may move accumulators right after them
