@@ -368,6 +368,224 @@ hipError_t launch_dv(const RouterArgs& a, bool xbf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Exactly 8 experts and D <= 4096: the whole W_r ([D][8] fp32, 128 KB) is
+// copied into LDS once, by asynchronous global->LDS copies, and x streams
+// through a ring of 4 chunks of 8 KB (32 tokens x 128 d bf16, or 64 d
+// fp32), also copied asynchronously, so that no register staging or
+// transposition sits between the loads and the chains. One lane per chain
+// (token tt, expert te); each 16 d take two (bf16) or four (fp32) 16-byte x
+// reads, shared by the token's 8 lanes, and eight paired W_r reads (8 lanes
+// read 8 consecutive floats), all in flight together. The x rows hold their
+// 16-byte groups at slot group ^ (token mod 8), so the 8 tokens of a wave
+// read 8 distinct bank groups. The ring is paced by explicit counter waits
+// and barriers, and the LDS reads wait for themselves, so that copies of
+// later chunks stay in flight while a chunk is summed.
+constexpr int kE8Tokens = 32;        // tokens per workgroup (4 waves)
+constexpr int kE8ChunkBytes = 8192;  // one x chunk
+constexpr int kE8Ring = 4;           // x chunks in the ring
+constexpr int kE8MaxD = 4096;        // W_r rows that fit beside the ring
+
+typedef float e8_f2 __attribute__((ext_vector_type(2)));
+typedef float e8_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned e8_u2 __attribute__((ext_vector_type(2)));
+typedef unsigned e8_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t e8_lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
+}
+__device__ __forceinline__ void lds_copy16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void router_e8_kernel(RouterArgs a) {
+  constexpr int SX = XBF16 ? 2 : 4;
+  constexpr int DKX = kE8ChunkBytes / (kE8Tokens * SX);  // d per chunk: 128 or 64
+  static_assert(kE8Ring == 4, "the chunk loop is unrolled for 4 ring slots");
+  // One array per ring slot, so that the compiler can tell a slot's reads
+  // from the copies still in flight into the other slots.
+  __shared__ __attribute__((aligned(16))) unsigned char wl[kE8MaxD * 32];
+  __shared__ __attribute__((aligned(16))) unsigned char xl0[kE8ChunkBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char xl1[kE8ChunkBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char xl2[kE8ChunkBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char xl3[kE8ChunkBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int te = tid & 7;   // expert
+  const int tt = tid >> 3;  // token in the workgroup
+  const int t0 = blockIdx.x * kE8Tokens;
+  const int D = a.D;
+  const int nch = (D + DKX - 1) / DKX;
+
+  // W_r copy: 16-byte pieces p = 256 i + tid of the D * 32 bytes
+  const int wpieces = D * 2;
+  const int wper = (wpieces + 255) / 256;  // the same for every thread
+  for (int i = 0; i < wper; ++i) {
+    const int p = min(256 * i + tid, wpieces - 1);
+    lds_copy16(reinterpret_cast<const unsigned char*>(a.W_r) + 16 * (size_t)p,
+               wl + 16 * (256 * i + 64 * wave));
+  }
+  // x chunk c -> its ring slot: LDS piece q = 64 (2 wave + r) + lane holds
+  // token q / 16, group (q % 16) ^ (token % 8)
+  auto issue_x = [&](int c, unsigned char* slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int q = 64 * (2 * wave + r) + lane;
+      const int tk = q >> 4, g = (q & 15) ^ (tk & 7);
+      const int t = min(t0 + tk, a.T - 1);
+      const int d = min(c * DKX + g * (16 / SX), D - 16 / SX);
+      lds_copy16(static_cast<const unsigned char*>(a.x) + ((size_t)t * D + d) * SX,
+                 slot + 1024 * (2 * wave + r));
+    }
+  };
+  if (0 < nch) issue_x(0, xl0);
+  if (1 < nch) issue_x(1, xl1);
+  if (2 < nch) issue_x(2, xl2);
+
+  float acc = 0.0f;
+  const unsigned char* wrow = wl + te * 4;
+  const int sw = tt & 7;
+  // one chunk from `slot`; the copies of chunk c + 3 go to `next`
+  auto chunk = [&](int c, const unsigned char* slot, unsigned char* next)
+      __attribute__((always_inline)) {
+    // chunk c (and the W_r copy, issued first) have landed once at most the
+    // later chunks' two copies per thread are in flight
+    const int ahead = min(kE8Ring - 2, nch - 1 - c);
+    if (ahead >= 2) wait_vm<4>();
+    else if (ahead == 1) wait_vm<2>();
+    else wait_vm<0>();
+    // every thread's copies of chunk c landed; every wave is done with the
+    // slot of chunk c - 1, which the copies of chunk c + 3 overwrite
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + kE8Ring - 1 < nch) issue_x(c + kE8Ring - 1, next);
+    const int dk = min(DKX, D - c * DKX);  // a multiple of 8
+    // The LDS reads sit in one asm block that waits for them itself: a
+    // plain load would make the compiler wait for every copy in flight,
+    // the ring's prefetch included.
+    const uint32_t xbase = e8_lds_addr(slot) + tt * 256;
+    uint32_t wa = e8_lds_addr(wrow) + (uint32_t)c * DKX * 32;
+    int dd = 0;
+    // 16 d per block: 8 W_r pairs and 16 x values in flight at once
+    for (; dd + 16 <= dk; dd += 16, wa += 512) {
+      const int g = dd / (16 / SX);
+      e8_f2 w[8];
+      float xv[16];
+      if (XBF16) {
+        e8_u4 u0, u1;
+        asm volatile(
+            "ds_read2_b32 %0, %10 offset1:8\n\t"
+            "ds_read2_b32 %1, %10 offset0:16 offset1:24\n\t"
+            "ds_read2_b32 %2, %10 offset0:32 offset1:40\n\t"
+            "ds_read2_b32 %3, %10 offset0:48 offset1:56\n\t"
+            "ds_read2_b32 %4, %10 offset0:64 offset1:72\n\t"
+            "ds_read2_b32 %5, %10 offset0:80 offset1:88\n\t"
+            "ds_read2_b32 %6, %10 offset0:96 offset1:104\n\t"
+            "ds_read2_b32 %7, %10 offset0:112 offset1:120\n\t"
+            "ds_read_b128 %8, %11\n\t"
+            "ds_read_b128 %9, %12\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(w[0]), "=v"(w[1]), "=v"(w[2]), "=v"(w[3]), "=v"(w[4]), "=v"(w[5]),
+              "=v"(w[6]), "=v"(w[7]), "=v"(u0), "=v"(u1)
+            : "v"(wa), "v"(xbase + ((g ^ sw) * 16)), "v"(xbase + (((g + 1) ^ sw) * 16)));
+        const unsigned uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          xv[2 * i] = __uint_as_float(uu[i] << 16);
+          xv[2 * i + 1] = __uint_as_float(uu[i] & 0xFFFF0000u);
+        }
+      } else {
+        e8_f4 f0, f1, f2, f3;
+        asm volatile(
+            "ds_read2_b32 %0, %12 offset1:8\n\t"
+            "ds_read2_b32 %1, %12 offset0:16 offset1:24\n\t"
+            "ds_read2_b32 %2, %12 offset0:32 offset1:40\n\t"
+            "ds_read2_b32 %3, %12 offset0:48 offset1:56\n\t"
+            "ds_read2_b32 %4, %12 offset0:64 offset1:72\n\t"
+            "ds_read2_b32 %5, %12 offset0:80 offset1:88\n\t"
+            "ds_read2_b32 %6, %12 offset0:96 offset1:104\n\t"
+            "ds_read2_b32 %7, %12 offset0:112 offset1:120\n\t"
+            "ds_read_b128 %8, %13\n\t"
+            "ds_read_b128 %9, %14\n\t"
+            "ds_read_b128 %10, %15\n\t"
+            "ds_read_b128 %11, %16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(w[0]), "=v"(w[1]), "=v"(w[2]), "=v"(w[3]), "=v"(w[4]), "=v"(w[5]),
+              "=v"(w[6]), "=v"(w[7]), "=v"(f0), "=v"(f1), "=v"(f2), "=v"(f3)
+            : "v"(wa), "v"(xbase + ((g ^ sw) * 16)), "v"(xbase + (((g + 1) ^ sw) * 16)),
+              "v"(xbase + (((g + 2) ^ sw) * 16)), "v"(xbase + (((g + 3) ^ sw) * 16)));
+        const e8_f4 ff[4] = {f0, f1, f2, f3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[4 * i] = ff[i].x;
+          xv[4 * i + 1] = ff[i].y;
+          xv[4 * i + 2] = ff[i].z;
+          xv[4 * i + 3] = ff[i].w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc = __builtin_fmaf(xv[2 * i], w[i].x, acc);
+        acc = __builtin_fmaf(xv[2 * i + 1], w[i].y, acc);
+      }
+    }
+    for (; dd < dk; dd += 4, wa += 128) {
+      const int g = dd / (16 / SX), within = (dd % (16 / SX)) * SX;
+      const uint32_t xa = xbase + ((g ^ sw) * 16) + within;
+      e8_f2 w01, w23;
+      float xv[4];
+      if (XBF16) {
+        e8_u2 u;
+        asm volatile(
+            "ds_read2_b32 %0, %3 offset1:8\n\t"
+            "ds_read2_b32 %1, %3 offset0:16 offset1:24\n\t"
+            "ds_read_b64 %2, %4\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(w01), "=v"(w23), "=v"(u)
+            : "v"(wa), "v"(xa));
+        xv[0] = __uint_as_float(u.x << 16);
+        xv[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        xv[2] = __uint_as_float(u.y << 16);
+        xv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        e8_f4 f;
+        asm volatile(
+            "ds_read2_b32 %0, %3 offset1:8\n\t"
+            "ds_read2_b32 %1, %3 offset0:16 offset1:24\n\t"
+            "ds_read_b128 %2, %4\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(w01), "=v"(w23), "=v"(f)
+            : "v"(wa), "v"(xa));
+        xv[0] = f.x;
+        xv[1] = f.y;
+        xv[2] = f.z;
+        xv[3] = f.w;
+      }
+      acc = __builtin_fmaf(xv[0], w01.x, acc);
+      acc = __builtin_fmaf(xv[1], w01.y, acc);
+      acc = __builtin_fmaf(xv[2], w23.x, acc);
+      acc = __builtin_fmaf(xv[3], w23.y, acc);
+    }
+  };
+  for (int c = 0; c < nch; c += 4) {
+    chunk(c, xl0, xl3);
+    if (c + 1 < nch) chunk(c + 1, xl1, xl0);
+    if (c + 2 < nch) chunk(c + 2, xl2, xl1);
+    if (c + 3 < nch) chunk(c + 3, xl3, xl2);
+  }
+
+  __syncthreads();  // every wave done with the ring
+  float* lg = reinterpret_cast<float*>(xl0);  // logit tile [32][8]
+  lg[tt * 8 + te] = acc;
+  __syncthreads();
+  select_topk<8, 1, 1>(a, lg, tt, te, t0);
+}
+
 template <int NE, int RE, int RT, int DK, int NTH = 256>
 hipError_t launch(const RouterArgs& a, bool xbf16, hipStream_t s) {
   constexpr int TB = (NTH / NE) * RT;
@@ -388,6 +606,12 @@ hipError_t launch_router(const moe_cfg& c, const void* x, const float* W_r, cons
   // (NE lanes per token, RE experts and RT tokens per lane, DK-deep chunks,
   // threads per workgroup): enough workgroups for every CU and at least two
   // waves per SIMD where the token count allows
+  if (c.E == 8 && c.D <= kE8MaxD) {
+    dim3 grid(ceil_div(c.T, kE8Tokens));
+    if (b) router_e8_kernel<true><<<grid, 256, 0, s>>>(a);
+    else router_e8_kernel<false><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (c.E <= 8) return launch_dv<8, 512, 128>(a, b, s);
   if (c.E <= 16) return launch_dv<16, 512, 128>(a, b, s);
   if (c.E <= 32) return launch<32, 1, 4, 64>(a, b, s);
