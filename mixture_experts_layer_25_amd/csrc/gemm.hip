@@ -46,7 +46,12 @@
 // middle of every odd step kt, certifies the copies of steps kt+1 and kt+2
 // and that every wave is done reading the stages of steps up to kt; each
 // step issues the copies of step kt - 1 + NSTAGE (into the stage of step
-// kt - 1), in two halves around a half-step's MFMAs.
+// kt - 1). The copy instructions sit between the MFMAs of the asm blocks
+// (an even step puts its copies into both of its blocks, an odd step all of
+// them after its barrier, where the stage of step kt - 1 becomes free), so
+// that a copy whose issue waits for room in the memory pipeline stalls
+// while the MFMA pipe is busy anyway; issued between the blocks, the copies
+// cost a fifth more cycles per step.
 //
 // Tile schedule (schedule_tile): the real tiles, in expert_tile_of order,
 // are cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD
@@ -56,6 +61,10 @@
 // workspace in a fixed order.
 #include "common.h"
 #include "launch.h"
+
+// The asm blocks that issue LDS copies set M0 themselves and list it as
+// clobbered; clang warns about clobbering a reserved register.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace moe {
 namespace {
@@ -422,6 +431,14 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   "v_mfma_f32_32x32x16_bf16 %[c21], %[a2], %[b1], %[c21]\n\t"                        \
   "v_mfma_f32_32x32x16_bf16 %[c30], %[a3], %[b0], %[c30]\n\t"                        \
   "v_mfma_f32_32x32x16_bf16 %[c31], %[a3], %[b1], %[c31]\n\t"
+// the MFMAs of G_MF with up to four copies between them (copy X: 16 bytes
+// per lane from global address %[gX] to LDS at M0 = %[mX] + 16 lane)
+#define G_MFI(I, J) "v_mfma_f32_32x32x16_bf16 %[c" #I #J "], %[a" #I "], %[b" #J "], %[c" #I #J "]\n\t"
+#define G_CP16(X) "s_mov_b32 m0, %[m" #X "]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[g" #X "], off\n\t"
+#define G_MF_CP(C0, C1, C2, C3)                                                      \
+  G_MFI(0, 0) C0 G_MFI(0, 1) G_MFI(1, 0) C1 G_MFI(1, 1) G_MFI(2, 0) C2 G_MFI(2, 1)     \
+  G_MFI(3, 0) C3 G_MFI(3, 1)
+#define G_NOCOPY [g0] "n"(0)
 #define G_RA                                                                         \
   "ds_read_b128 %[na0], %[aa]\n\t"                                                   \
   "ds_read_b128 %[na1], %[aa] offset:2048\n\t"                                       \
@@ -445,7 +462,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   // MXFP4 codes at BA0/BA1 + MXOFF, scales at SA0/SA1) while the MFMAs
   // (string MF) consume set C; then set N's B fragments are assembled or
   // converted
-#define G_BLOCK(OFF0, OFF1, MXOFF, AA, BA0, BA1, SA0, SA1, N, C, MF)                 \
+#define G_BLOCK(OFF0, OFF1, MXOFF, AA, BA0, BA1, SA0, SA1, N, C, MF, ...)            \
   do {                                                                               \
     if (!MX) {                                                                       \
       asm volatile("s_nop 4\n\t" G_RA                                                \
@@ -456,8 +473,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
                      [h2] "=&v"(h2), [h3] "=&v"(h3), G_ACC                           \
                    : [a0] "v"(C##a0), [a1] "v"(C##a1), [a2] "v"(C##a2),               \
                      [a3] "v"(C##a3), [b0] "v"(C##b0), [b1] "v"(C##b1),               \
-                     [aa] "v"(AA), [ba0] "v"(BA0), [ba1] "v"(BA1)                     \
-                   : "memory");                                                      \
+                     [aa] "v"(AA), [ba0] "v"(BA0), [ba1] "v"(BA1), __VA_ARGS__        \
+                   : "memory", "m0");                                                \
       const s16x8_t v0 = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};   \
       const s16x8_t v1 = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};   \
       N##b0 = __builtin_bit_cast(bf16x8_t, v0);                                      \
@@ -471,8 +488,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
                    : [a0] "v"(C##a0), [a1] "v"(C##a1), [a2] "v"(C##a2),               \
                      [a3] "v"(C##a3), [b0] "v"(C##b0), [b1] "v"(C##b1),               \
                      [aa] "v"(AA), [ba0] "v"(BA0), [ba1] "v"(BA1), [sa0] "v"(SA0),    \
-                     [sa1] "v"(SA1)                                                  \
-                   : "memory");                                                      \
+                     [sa1] "v"(SA1), __VA_ARGS__                                     \
+                   : "memory", "m0");                                                \
       N##b0 = mx_fragment(cw0, sw0);                                                 \
       N##b1 = mx_fragment(cw1, sw1);                                                 \
     }                                                                                \
@@ -546,11 +563,70 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     int kt = 0;
     uint32_t so = 0;                         // byte offset of stage kt % NST
     uint32_t si = (uint32_t)(NST - 1) * SB;  // stage of step kt - 1 + NST
+    auto next_stage = [](uint32_t o) { return o + SB == NST * SB ? 0u : o + SB; };
+    {
+      // Pairs of steps (kt even, kt + 1 odd) that both issue copies, with
+      // the copies inside the asm blocks. Copy destinations (M0): A copy r
+      // of wave w at stage + 8192 r + 1024 w, bf16 B copy r at stage +
+      // A_BYTES + 2048 w + 1024 r. (MXFP4 B copies, one per thread and step,
+      // of a size that depends on the wave, stay between the blocks.)
+      const uint32_t lds_a = __builtin_amdgcn_readfirstlane(smem_addr + wave * 1024);
+      const uint32_t lds_b = __builtin_amdgcn_readfirstlane(smem_addr + A_BYTES + wave * 2048);
+      for (; kt + NST < nk; kt += 2) {
+        const uint32_t so1 = next_stage(so), so2 = next_stage(so1), si1 = next_stage(si);
+        // step kt: copies of step kt - 1 + NST into the stage of step kt - 1
+        int is = kt - 1 + NST;
+        uint64_t ga0 = (uint64_t)(a_g[0] + is * BK), ga1 = (uint64_t)(a_g[1] + is * BK);
+        G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
+                s_addr[0] + so, s_addr[1] + so, y, x, G_MF_CP(G_CP16(0), "", G_CP16(1), ""),
+                [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si), [m1] "s"(lds_a + si + 8192));
+        if (!MX) {
+          const uint64_t gb0 = (uint64_t)(b_g[0] + (size_t)is * BK * N * 2);
+          const uint64_t gb1 = (uint64_t)(b_g[1] + (size_t)is * BK * N * 2);
+          G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
+                  s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF_CP(G_CP16(0), "", G_CP16(1), ""),
+                  [g0] "v"(gb0), [g1] "v"(gb1), [m0] "s"(lds_b + si), [m1] "s"(lds_b + si + 1024));
+        } else {
+          G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
+                  s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF, G_NOCOPY);
+          issue_b(is, si);
+        }
+        // step kt + 1: after the barrier, copies of step kt + NST into the
+        // stage of step kt
+        G_BLOCK("8192", "10240", "8", a_addr[1] + so1, b_addr[0] + so1, b_addr[1] + so1,
+                s_addr[0] + so1, s_addr[1] + so1, y, x, G_MF, G_NOCOPY);
+        wait_vmcnt<PER * (NST - 4)>();  // steps up to kt + 3 have landed
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        is = kt + NST;
+        ga0 = (uint64_t)(a_g[0] + is * BK);
+        ga1 = (uint64_t)(a_g[1] + is * BK);
+        if (!MX) {
+          const uint64_t gb0 = (uint64_t)(b_g[0] + (size_t)is * BK * N * 2);
+          const uint64_t gb1 = (uint64_t)(b_g[1] + (size_t)is * BK * N * 2);
+          G_BLOCK("0", "2048", "0", a_addr[0] + so2, b_addr[0] + so2, b_addr[1] + so2,
+                  s_addr[0] + so2, s_addr[1] + so2, x, y,
+                  G_MF_CP(G_CP16(0), G_CP16(1), G_CP16(2), G_CP16(3)),
+                  [g0] "v"(ga0), [g1] "v"(ga1), [g2] "v"(gb0), [g3] "v"(gb1),
+                  [m0] "s"(lds_a + si1), [m1] "s"(lds_a + si1 + 8192), [m2] "s"(lds_b + si1),
+                  [m3] "s"(lds_b + si1 + 1024));
+        } else {
+          G_BLOCK("0", "2048", "0", a_addr[0] + so2, b_addr[0] + so2, b_addr[1] + so2,
+                  s_addr[0] + so2, s_addr[1] + so2, x, y, G_MF_CP(G_CP16(0), "", G_CP16(1), ""),
+                  [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si1),
+                  [m1] "s"(lds_a + si1 + 8192));
+          issue_b(is, si1);
+        }
+        so = so2;
+        si = next_stage(si1);
+      }
+    }
+    // the remaining steps: copies (while any are left) between the blocks
     for (; kt + 1 < nk; ++kt) {
       const uint32_t so1 = so + SB == NST * SB ? 0u : so + SB;
       const int is = kt - 1 + NST;  // step whose copies this iteration issues
       G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
-              s_addr[0] + so, s_addr[1] + so, y, x, G_MF);
+              s_addr[0] + so, s_addr[1] + so, y, x, G_MF, G_NOCOPY);
       if (kt & 1) {
         // certify steps kt+1 and kt+2; every wave is done with steps < kt+1
         wait_copy_groups<PER>(min(nk - 1, kt - 2 + NST) - min(kt + 2, nk - 1));
@@ -559,15 +635,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
       }
       if (is < nk) issue_a(is, si);
       G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
-              s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF);
+              s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF, G_NOCOPY);
       if (is < nk) issue_b(is, si);
       so = so1;
-      si = si + SB == NST * SB ? 0u : si + SB;
+      si = next_stage(si);
     }
     // last step; these blocks end with the MFMA result wait states since
     // the compiler may move accumulators right after them
     G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
-            s_addr[0] + so, s_addr[1] + so, y, x, G_MF MFMA_TAIL);
+            s_addr[0] + so, s_addr[1] + so, y, x, G_MF MFMA_TAIL, G_NOCOPY);
     G_MMA(G_MF MFMA_TAIL);
   }
   // the last MFMAs finish writing the accumulators before any VALU reads them
