@@ -725,11 +725,13 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
         const int m = 32 * i + 8 * (r >> 2) + 4 * lq + (r & 3);
         float g = acc[i][0][r], u = acc[i][1][r];
         if (clampit) {
-          g = clampf(g, a.clamp);
-          u = clampf(u, a.clamp);
+          g = __builtin_amdgcn_fmed3f(g, -a.clamp, a.clamp);
+          u = __builtin_amdgcn_fmed3f(u, -a.clamp, a.clamp);
         }
-        *reinterpret_cast<uint16_t*>(wl + m * 64 + lrow * 2) =
-            static_cast<uint16_t>(f32_to_bf16(silu_f32(g) * u));
+        // SiLU(g) u with the hardware exp2 and reciprocal (about 1 ulp
+        // each) and the hardware round-to-nearest-even bf16 conversion
+        const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        *reinterpret_cast<__bf16*>(wl + m * 64 + lrow * 2) = (__bf16)h;
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own wave's tile only
