@@ -16,8 +16,8 @@
 //          base rank, and the expert's total count;
 //   rank:  per chunk, kept counts -> offsets (every workgroup rescans the
 //          E counts; E <= 1024), then each pair's rank = chunk base + earlier
-//          waves' counts + earlier pairs in the wave (a broadcast scan over
-//          LDS) -> slot_pos, perm_token;
+//          waves' counts + earlier pairs in the wave (per-expert lane masks
+//          in LDS) -> slot_pos, perm_token;
 //   copy:  one wave per token reads the row once (16-byte vectors) and
 //          writes it to each kept slot.
 #include "common.h"
@@ -72,8 +72,9 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot_pos, int32_t* __restrict__ perm) {
   __shared__ int off_sh[kMaxE + 1];
   __shared__ int wh[4][kMaxE];
-  __shared__ int idx_sh[256][kMaxK];
   __shared__ int wave_tot[4];
+  __shared__ int ev_sh[256][kMaxK + 1];
+  __shared__ unsigned long long lanes_of[4][kMaxE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -97,6 +98,10 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
     wh[1][e] = 0;
     wh[2][e] = 0;
     wh[3][e] = 0;
+    lanes_of[0][e] = 0ull;
+    lanes_of[1][e] = 0ull;
+    lanes_of[2][e] = 0ull;
+    lanes_of[3][e] = 0ull;
   }
   __syncthreads();
   int base = incl - local;
@@ -109,34 +114,61 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
   }
   if (tid == 255) off_sh[E] = base;  // total kept (thread 255 covers e >= E - 1)
 
-  // this chunk's pairs: LDS copy and per-wave histograms
+  // this token's pairs (e = -1: none) and the per-wave histograms
   const int t = chunk * kChunk + tid;
   const bool valid_t = t < T;
-  for (int j = 0; j < k; ++j) {
-    const int e = valid_t ? idx[(size_t)t * k + j] : -1;
-    idx_sh[tid][j] = e;
-    if (e >= 0 && e < E) atomicAdd(&wh[wave][e], 1);
+  int ev[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    int e = -1;
+    if (j < k && valid_t) {
+      e = idx[(size_t)t * k + j];
+      if (e < 0 || e >= E) e = -1;
+    }
+    ev[j] = e;
+    ev_sh[tid][j] = e;
+    if (e >= 0) atomicAdd(&wh[wave][e], 1);
   }
   __syncthreads();
   if (chunk == 0) {
     for (int e = tid; e <= E; e += 256) offsets[e] = off_sh[e];
   }
+
+  // Pairs of earlier tokens of this wave with the same expert, column by
+  // column: every lane sets its bit in the mask of its column-jj expert,
+  // then each pair counts the set bits of lanes below it in the mask of its
+  // own expert, and the lanes clear what they set. (A wave's LDS
+  // instructions run in program order.)
+  const uint64_t below = (1ull << lane) - 1ull;
+  int r[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) r[j] = 0;
+  for (int jj = 0; jj < k; ++jj) {
+    const int col = ev_sh[tid][jj];
+    if (col >= 0)
+      __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(&lanes_of[wave][col]) + (lane >> 5),
+                            1u << (lane & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k && ev[j] >= 0) r[j] += __popcll(lanes_of[wave][ev[j]] & below);
+    if (col >= 0) lanes_of[wave][col] = 0ull;
+  }
   if (!valid_t) return;
 
-  for (int j = 0; j < k; ++j) {
-    const int e = idx_sh[tid][j];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) continue;
+    const int e = ev[j];
     int slot = -1;
-    if (e >= 0 && e < E) {
-      int r = chunk_ws[(size_t)e * nchunks + chunk];
-      for (int w = 0; w < wave; ++w) r += wh[w][e];
-      // earlier tokens of this wave
-      const int* wbase = &idx_sh[wave * 64][0];
-      for (int l = 0; l < lane; ++l)
-        for (int jj = 0; jj < k; ++jj) r += (wbase[l * kMaxK + jj] == e);
+    if (e >= 0) {
+      int rank = chunk_ws[(size_t)e * nchunks + chunk] + r[j];
+      for (int w = 0; w < wave; ++w) rank += wh[w][e];
       // earlier slots of this token
-      for (int jj = 0; jj < j; ++jj) r += (idx_sh[tid][jj] == e);
-      if (capacity <= 0 || r < capacity) {
-        slot = off_sh[e] + r;
+#pragma unroll
+      for (int jj = 0; jj < kMaxK; ++jj)
+        if (jj < j) rank += (ev[jj] == e);
+      if (capacity <= 0 || rank < capacity) {
+        slot = off_sh[e] + rank;
         perm[slot] = t;
       }
     }
