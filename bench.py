@@ -82,7 +82,7 @@ def roofline_kernel(cfg):
         return {"name": "ffn_f32_gateup_kernel", "src": "ffn_f32.hip", "bound": "alu"}
     if cfg.wdt == 2:
         return {"name": "gemm_kernel<0, true>", "src": "gemm.hip", "bound": "mfma"}
-    return {"name": "gemm_bf16_kernel<0>", "src": "gemm.hip", "bound": "mfma"}
+    return {"name": "gemm_kernel<0, false>", "src": "gemm.hip", "bound": "mfma"}
 
 
 def src_sha256(name):
