@@ -25,11 +25,15 @@
  *   W_r      [D][E]      fp32
  *   bias     [E]         fp32
  *   W_gate, W_up [E][D][F]  and  W_down [E][F][D]   w dtype F32 or BF16
- *   MXFP4 weights keep the logical [E][K][N] matrix but are stored
- *     K-contiguous per output column n: codes uint8 [E][N][K/2] (element
- *     2i in the low nibble, 2i+1 in the high nibble), e8m0 scales uint8
- *     [E][N][K/32] (scale 2^(s-127), s = 255 not allowed); for gate/up
- *     K = D, N = F; for down K = F, N = D (OCP MX v1.0 e2m1 + e8m0).
+ *   MXFP4 weights keep the logical [E][K][N] matrix but are stored by
+ *     32-element K-blocks (the MX scaling blocks), block-major: codes uint8
+ *     [E][K/32][N][16] (the 16 bytes of block b of column n; element 2i of
+ *     the block in the low nibble of byte i, 2i+1 in the high nibble),
+ *     e8m0 scales uint8 [E][K/32][N] (scale 2^(s-127), s = 255 not
+ *     allowed); for gate/up K = D, N = F; for down K = F, N = D (OCP MX
+ *     v1.0 e2m1 + e8m0). Block-major storage puts one K-block of
+ *     consecutive columns in consecutive bytes, so the GEMM's per-step
+ *     copies read whole cache lines.
  *   Shared expert: Ws_gate, Ws_up [D][shared_F], Ws_down [shared_F][D], bf16.
  *   topk_idx int32 [T][k], topk_w fp32 [T][k]   (slot 0 = largest key)
  *   counts   int32 [E]      pairs routed to each expert, before capacity

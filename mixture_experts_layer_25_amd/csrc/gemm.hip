@@ -30,7 +30,10 @@
 //   is read with the gfx950 transposing LDS load ds_read_b64_tr_b16 (within
 //   a 16-lane group, lane i receives element i of the 4 rows the group
 //   points at), two per fragment, so no transpose runs on the vector ALUs.
-//   B MXFP4 (codes K-contiguous per column): each column's 16 code bytes of
+//   B MXFP4 (stored by 32-k blocks, block-major, so that a step's codes of
+//   consecutive columns are consecutive 16-byte pieces; stored K-contiguous
+//   per column, every copy lane touched its own cache line and the B
+//   copies cost a quarter of the step): each column's 16 code bytes of
 //   the step and its e8m0 scale are copied to LDS; a lane reads the 4 code
 //   bytes of its k-group and the scale and converts them exactly to bf16
 //   with v_cvt_scalef32_pk_bf16_fp4 (fp32 products for the scale codes at
@@ -329,12 +332,14 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   } else {
     bool up;
     const int col = b_column(64 * (wave & 3) + lane, up);
+    // block-major storage: step kt's codes of column col at
+    // ((e K/32 + kt) N + col) 16, its scale at (e K/32 + kt) N + col
     if (wave < 4) {
       const uint8_t* base = static_cast<const uint8_t*>(up ? a.B1 : a.B0);
-      b_g[0] = base + ((size_t)e * N + col) * (K / 2) + kt_begin * (BK / 2);
+      b_g[0] = base + (((size_t)e * (K / 32) + kt_begin) * N + col) * 16;
     } else {
       const uint8_t* base = up ? a.S1 : a.S0;
-      b_g[0] = base + ((size_t)e * N + col) * (K / 32) + kt_begin;
+      b_g[0] = base + ((size_t)e * (K / 32) + kt_begin) * N + col;
     }
     b_g[1] = nullptr;
   }
@@ -351,9 +356,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
       dma16(b_g[0] + step, Bs + (4 * wave) * 512);
       dma16(b_g[1] + step, Bs + (4 * wave + 2) * 512);
     } else if (wave < 4) {
-      dma16(b_g[0] + kt * (BK / 2), Bs + wave * 1024);
+      dma16(b_g[0] + (size_t)kt * N * 16, Bs + wave * 1024);
     } else {
-      dma1(b_g[0] + kt, Bs + MXC_BYTES + (wave - 4) * 256);
+      dma1(b_g[0] + (size_t)kt * N, Bs + MXC_BYTES + (wave - 4) * 256);
     }
   };
 

@@ -164,9 +164,9 @@ class Inputs:
     W_gate: np.ndarray | None = None   # [E, D, F] f32/u16
     W_up: np.ndarray | None = None     # [E, D, F]
     W_down: np.ndarray | None = None   # [E, F, D]
-    S_gate: np.ndarray | None = None   # MXFP4: codes [E,F,D/2] in W_gate, scales [E,F,D/32]
+    S_gate: np.ndarray | None = None   # MXFP4: codes [E,D/32,F,16] in W_gate, scales [E,D/32,F]
     S_up: np.ndarray | None = None
-    S_down: np.ndarray | None = None   # MXFP4: codes [E,D,F/2] in W_down, scales [E,D,F/32]
+    S_down: np.ndarray | None = None   # MXFP4: codes [E,F/32,D,16] in W_down, scales [E,F/32,D]
     Ws_gate: np.ndarray | None = None  # [D, Fs] u16
     Ws_up: np.ndarray | None = None
     Ws_down: np.ndarray | None = None  # [Fs, D] u16
@@ -195,13 +195,16 @@ def make_bias(cfg: Config, seed: int = 0) -> np.ndarray | None:
 def make_expert_weights(cfg: Config, tid: int, K: int, N: int, seed: int = 0,
                         pool: ThreadPoolExecutor | None = None):
     """Per-expert [K, N] weights (logical layout). For MXFP4, returns
-    (codes [E,N,K/2], scales [E,N,K/32]); else one [E,K,N] array."""
+    (codes [E,K/32,N,16], scales [E,K/32,N]), stored by 32-element K-blocks,
+    block-major; else one [E,K,N] array."""
     E = cfg.E
 
     def one(e):
         w = _normal(seed, tid, e, K * N, cfg.w_sigma).reshape(K, N)
         if cfg.wdt == MXFP4:
-            return quantize_mxfp4_rows(np.ascontiguousarray(w.T))
+            codes, scales = quantize_mxfp4_rows(np.ascontiguousarray(w.T))
+            return (np.ascontiguousarray(codes.reshape(N, K // 32, 16).transpose(1, 0, 2)),
+                    np.ascontiguousarray(scales.T))
         return _act_encode(w, cfg.wdt)
 
     own = pool is None

@@ -122,15 +122,17 @@ static float act_f32(const oracle_cfg* c, const void* x, size_t i) {
 static double wt(const oracle_cfg* c, const void* W, const uint8_t* S, int e,
                  int K, int N, int kk, int n) {
   /* Logical weight element W[e][kk][n] of a [E][K][N] matrix. MXFP4 storage
-   * is K-contiguous per output column: codes [E][N][K/2], scales
-   * [E][N][K/32]. */
+   * is by 32-element K-blocks, block-major: codes [E][K/32][N][16] (byte i
+   * of a block holds elements 2i, low nibble, and 2i+1), scales
+   * [E][K/32][N]. */
   if (c->wdt == OR_F32) return ((const float*)W)[((size_t)e * K + kk) * N + n];
   if (c->wdt == OR_BF16)
     return oracle_bf16_to_double(((const uint16_t*)W)[((size_t)e * K + kk) * N + n]);
   const uint8_t* codes = (const uint8_t*)W;
-  uint8_t byte = codes[((size_t)e * N + n) * (K / 2) + kk / 2];
+  const size_t blk = ((size_t)e * (K / 32) + kk / 32) * N + n;
+  uint8_t byte = codes[blk * 16 + (kk % 32) / 2];
   unsigned code = (kk & 1) ? (byte >> 4) : (byte & 15u);
-  unsigned s = S[((size_t)e * N + n) * (K / 32) + kk / 32];
+  unsigned s = S[blk];
   return oracle_e2m1(code) * oracle_e8m0(s);
 }
 

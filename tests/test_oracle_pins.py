@@ -364,8 +364,12 @@ def _dense_swiglu_np(x, Wg, Wu, Wd, clamp=0.0, round_h=None):
 
 
 def _decode_mx(codes, scales):
-    """[N, K/2] codes, [N, K/32] scales -> float64 [K, N] (test-side decoder)."""
+    """[K/32, N, 16] codes, [K/32, N] scales (32-element K-blocks,
+    block-major) -> float64 [K, N] (test-side decoder)."""
     tab = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+    nb, n_cols, _ = codes.shape
+    codes = codes.transpose(1, 0, 2).reshape(n_cols, nb * 16)
+    scales = scales.T
     lo = tab[codes & 15]
     hi = tab[codes >> 4]
     N, K2 = codes.shape
