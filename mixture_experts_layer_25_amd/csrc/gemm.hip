@@ -133,25 +133,42 @@ __device__ __forceinline__ float e8m0_scale(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-// 8 e2m1 codes (k-consecutive, low nibble first) and their e8m0 scale ->
-// one MFMA fragment of 8 bf16. The hardware conversion multiplies by the
-// fp32 scale exactly for scale codes 2..252; outside that range (tiny or
-// huge blocks) the products are formed in fp32.
-__device__ __forceinline__ bf16x8_t mx_fragment(uint32_t codes, uint32_t s) {
-  const float sc = e8m0_scale(s);
-  u32x4_t o;
-  if (s >= 2u && s <= 252u) {
-    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
-    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
-    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
-    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+// Two fragments (8 e2m1 codes each, k-consecutive, low nibble first, with
+// their e8m0 scales) -> two MFMA fragments of 8 bf16. The hardware
+// conversion multiplies by the fp32 scale exactly for scale codes 2..252,
+// where 2^(s - 127) is the float with exponent field s; when either code is
+// outside that range (tiny or huge blocks) both fragments are formed from
+// fp32 products instead. One range test serves both fragments.
+template <int I>
+__device__ __forceinline__ uint32_t mx_cvt(uint32_t codes, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, I));
+}
+__device__ __forceinline__ void mx_fragments(uint32_t c0, uint32_t s0, uint32_t c1, uint32_t s1,
+                                             bf16x8_t& f0, bf16x8_t& f1) {
+  u32x4_t o0, o1;
+  if (max(s0 - 2u, s1 - 2u) < 251u) {
+    const float a0 = __uint_as_float(s0 << 23), a1 = __uint_as_float(s1 << 23);
+    o0.x = mx_cvt<0>(c0, a0);
+    o0.y = mx_cvt<1>(c0, a0);
+    o0.z = mx_cvt<2>(c0, a0);
+    o0.w = mx_cvt<3>(c0, a0);
+    o1.x = mx_cvt<0>(c1, a1);
+    o1.y = mx_cvt<1>(c1, a1);
+    o1.z = mx_cvt<2>(c1, a1);
+    o1.w = mx_cvt<3>(c1, a1);
   } else {
-    o.x = mx_pair(codes & 0xFFu, sc);
-    o.y = mx_pair((codes >> 8) & 0xFFu, sc);
-    o.z = mx_pair((codes >> 16) & 0xFFu, sc);
-    o.w = mx_pair(codes >> 24, sc);
+    const float a0 = e8m0_scale(s0), a1 = e8m0_scale(s1);
+    o0.x = mx_pair(c0 & 0xFFu, a0);
+    o0.y = mx_pair((c0 >> 8) & 0xFFu, a0);
+    o0.z = mx_pair((c0 >> 16) & 0xFFu, a0);
+    o0.w = mx_pair(c0 >> 24, a0);
+    o1.x = mx_pair(c1 & 0xFFu, a1);
+    o1.y = mx_pair((c1 >> 8) & 0xFFu, a1);
+    o1.z = mx_pair((c1 >> 16) & 0xFFu, a1);
+    o1.w = mx_pair(c1 >> 24, a1);
   }
-  return __builtin_bit_cast(bf16x8_t, o);
+  f0 = __builtin_bit_cast(bf16x8_t, o0);
+  f1 = __builtin_bit_cast(bf16x8_t, o1);
 }
 
 // Slot permutation of the 4 k-groups of a 64-byte A row: rows r..r+15 then
@@ -495,8 +512,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
                      [aa] "v"(AA), [ba0] "v"(BA0), [ba1] "v"(BA1), [sa0] "v"(SA0),    \
                      [sa1] "v"(SA1), __VA_ARGS__                                     \
                    : "memory", "m0");                                                \
-      N##b0 = mx_fragment(cw0, sw0);                                                 \
-      N##b1 = mx_fragment(cw1, sw1);                                                 \
+      mx_fragments(cw0, sw0, cw1, sw1, N##b0, N##b1);                                \
     }                                                                                \
   } while (0)
   // MFMAs only, on set y (the last half-step)
@@ -556,8 +572,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
                    : [aa] "v"(a_addr[0]), [ba0] "v"(b_addr[0]), [ba1] "v"(b_addr[1]),
                      [sa0] "v"(s_addr[0]), [sa1] "v"(s_addr[1])
                    : "memory");
-      xb0 = mx_fragment(cw0, sw0);
-      xb1 = mx_fragment(cw1, sw1);
+      mx_fragments(cw0, sw0, cw1, sw1, xb0, xb1);
     }
 
     // Step kt: (kt, 1) is read into set y while (kt, 0) multiplies set x;

@@ -81,6 +81,24 @@ def test_clamp_saturation_and_mxfp4_shared():
     assert np.any(np.abs(h) > 50)
 
 
+def test_mxfp4_scale_codes_at_the_range_ends():
+    """Blocks whose e8m0 scale code lies outside 2..252 take the fp32-product
+    conversion (with their neighbours in the same fragment pair): tiny
+    scales 0 and 1, and the largest codes 253, 254 on blocks of zero codes
+    (so the products stay finite)."""
+    cfg = syn.Config("mxscale", T=160, D=128, E=8, k=2, F=64, wdt=syn.MXFP4,
+                     gating=syn.GATE_SOFTMAX, renorm=1, bias="normal", bias_sigma=0.3)
+    inp = syn.make_inputs(cfg)
+    for S, W in ((inp.S_gate, inp.W_gate), (inp.S_up, inp.W_up), (inp.S_down, inp.W_down)):
+        # storage: codes [E][K/32][N][16], scales [E][K/32][N]
+        S[:, 0, 0:8] = 0
+        S[:, 0, 8:16] = 1
+        S[:, 1, 16:20] = 253
+        S[:, 1, 20:24] = 254
+        W[:, 1, 16:24, :] = 0
+    _run(cfg, inp)
+
+
 def test_sigmoid_renorm_fp32():
     cfg = syn.Config("sigfp32", T=130, D=64, E=6, k=3, F=40, act=syn.F32, wdt=syn.F32,
                      gating=syn.GATE_SIGMOID, renorm=1, bias="normal", bias_sigma=0.3)
