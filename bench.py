@@ -55,6 +55,10 @@ def parse():
                     help="write profiles/hbm_traffic_<workload>.{json,txt} from two --pmc runs")
     ap.add_argument("--profile-command", default="",
                     help="the command that produced the profile, recorded in the summary")
+    ap.add_argument("--study", choices=["dense-vs-moe", "topk"],
+                    help="instead of the layer benchmark: the dense layer against an MoE of "
+                         "single-linear experts, or the top-k 1/2/4 sweep (one JSON line per "
+                         "measurement)")
     return ap.parse_args()
 
 
@@ -183,8 +187,125 @@ def pct(vals, q):
     return v[i]
 
 
+def _time_steps(fns, steps, warmup, stream):
+    """Per-step times (ms) of running fns in order, with an event between
+    the stages; returns (per_step_ms, per_stage_mean_ms)."""
+    import torch
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for evs in ev:
+        evs[0].record(stream)
+        for i, fn in enumerate(fns):
+            fn()
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = [evs[0].elapsed_time(evs[-1]) for evs in ev]
+    per_stage = [sum(evs[i].elapsed_time(evs[i + 1]) for evs in ev) / steps for i in range(len(fns))]
+    return per_step, per_stage
+
+
+def study_dense_vs_moe(args):
+    """The pages' dense-versus-MoE comparison (S = 4096, D = 4096, 8 experts,
+    top-2; dense 4096 x 4096, experts 4096 x 512) on this GPU."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_25_amd import moe, studies, synthetic as syn
+
+    T, D, E, k, n_out = 4096, 4096, 8, 2, 512
+    x_h, W_r_h, W_lin_h, W_dense_h = syn.make_linear_layer_inputs(T, D, E, n_out)
+    dev = "cuda"
+    x = torch.from_numpy(x_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    W_r = torch.from_numpy(W_r_h).to(dev)
+    W_lin = torch.from_numpy(W_lin_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    W_dense = torch.from_numpy(W_dense_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    cfg = moe.make_cfg(T=T, D=D, E=E, F=n_out, top_k=k, gating="softmax", renorm=True)
+    lin = studies.LinearMoE(cfg, x, W_r, None, W_lin)
+    dense = studies.DenseLinear(x, W_dense)
+    stream = torch.cuda.current_stream()
+    names = [n for n, _ in lin.stages()]
+    moe_steps, moe_stages = _time_steps([f for _, f in lin.stages()], args.steps, args.warmup, stream)
+    dense_steps, _ = _time_steps([dense], args.steps, args.warmup, stream)
+    moe_ms = float(np.mean(moe_steps))
+    dense_ms = float(np.mean(dense_steps))
+    rec = {"study": "dense_vs_moe", "tokens": T, "D": D, "experts": E, "top_k": k,
+           "expert_shape": [D, n_out], "dense_shape": [D, D], "dtype": "bf16",
+           "dense_ms": round(dense_ms, 4), "moe_ms": round(moe_ms, 4),
+           "dense_over_moe": round(dense_ms / moe_ms, 3),
+           "moe_stage_ms": {n: round(v, 4) for n, v in zip(names, moe_stages)},
+           "dense_tflops": round(2.0 * T * D * D / (dense_ms * 1e-3) / 1e12, 1),
+           "activated_params": {"dense": D * D, "moe": k * D * n_out},
+           "pages_ascend910": {"dense": 2.8, "moe": 1.5, "units": "unstated"},
+           "steps": args.steps, "data": "synthetic"}
+    print(json.dumps(rec), flush=True)
+
+
+def study_topk(args):
+    """Per-token time at top-k 1, 2, 4 on the fine-grained layer with the
+    shared expert (the MXFP4 layer's architecture, T = 16384)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_25_amd import moe, synthetic as syn, upload
+
+    base = syn.CONFIGS["fine384_mxfp4"]
+    inp = syn.make_inputs(base)
+    c0, x, W_r, bias, w = upload.to_device(inp)
+    del inp
+    stream = torch.cuda.current_stream()
+    wstruct = w.struct()
+    for k in (1, 2, 4):
+        c = moe.make_cfg(T=base.T, D=base.D, E=base.E, F=base.F, top_k=k, gating=base.gating,
+                         renorm=bool(base.renorm), capacity=base.capacity, clamp=base.clamp,
+                         act=base.act, w=base.wdt, shared_F=base.shared_F)
+        ws = moe.workspace(c, moe.WS_FORWARD, x.device)
+        y = torch.empty((base.T, base.D), dtype=torch.bfloat16, device=x.device)
+        idx = torch.empty((base.T, k), dtype=torch.int32, device=x.device)
+        tw = torch.empty((base.T, k), dtype=torch.float32, device=x.device)
+        counts = torch.empty(base.E, dtype=torch.int32, device=x.device)
+        offsets = torch.empty(base.E + 1, dtype=torch.int32, device=x.device)
+
+        def fwd():
+            moe.forward(c, x, W_r, bias, w, y=y, ws=ws, topk_idx=idx, topk_w=tw, counts=counts,
+                        offsets=offsets, wstruct=wstruct)
+        steps, _ = _time_steps([fwd], args.steps, args.warmup, stream)
+        per_tok_us = [1e3 * ms / base.T for ms in steps]
+        kept = int(offsets[-1].item())
+        # the shared expert is added once: y(with) - y(without) against its own output
+        c_ns = moe.make_cfg(T=base.T, D=base.D, E=base.E, F=base.F, top_k=k, gating=base.gating,
+                            renorm=bool(base.renorm), capacity=base.capacity, clamp=base.clamp,
+                            act=base.act, w=base.wdt, shared_F=0)
+        y_ns = moe.forward(c_ns, x, W_r, bias, w)
+        _, y_sh = moe.shared_expert(c, x, w)
+        torch.cuda.synchronize()
+        diff = (y.float() - y_ns.float()).double()
+        sh = y_sh[:base.T].double()
+        # least-squares coefficient of y(with) - y(without) on the shared
+        # output: 1 when it is added once, 2 if it were added twice
+        scale = float((diff * sh).sum() / (sh * sh).sum())
+        # residual against two bf16 roundings of the outputs
+        lim = 2e-2 * torch.clamp(sh.abs(), min=1.0) + 2.0 ** -7 * y.double().abs()
+        within = bool(((diff - sh).abs() <= lim).all())
+        rec = {"study": "topk_sweep", "layer": "fine384_mxfp4 architecture, T=16384, shared expert",
+               "top_k": k, "ms_per_step_mean": round(float(np.mean(steps)), 4),
+               "per_token_us": {"p50": round(pct(per_tok_us, 50), 5), "p95": round(pct(per_tok_us, 95), 5),
+                                "p99": round(pct(per_tok_us, 99), 5)},
+               "kept_pairs": kept, "top_misses": base.T * k - kept,
+               "shared_output_coefficient": round(scale, 6), "shared_within_rounding": within,
+               "steps": args.steps, "data": "synthetic"}
+        print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
+    if args.study:
+        if args.gpus != 1:
+            print("the studies run on one GPU", file=sys.stderr)
+            sys.exit(2)
+        return study_dense_vs_moe(args) if args.study == "dense-vs-moe" else study_topk(args)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args.workload, args.profile_command)
     if args.summarize_pmc:

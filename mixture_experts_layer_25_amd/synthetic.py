@@ -222,6 +222,19 @@ def make_expert_weights(cfg: Config, tid: int, K: int, N: int, seed: int = 0,
     return np.stack(parts)
 
 
+def make_linear_layer_inputs(T: int, D: int, E: int, n_out: int, seed: int = 0,
+                             x_sigma: float = 1.0, wr_sigma: float = 0.02, w_sigma: float = 0.02):
+    """Inputs of the dense-versus-MoE comparison with single-linear experts:
+    x [T, D] bf16 bits, W_r [D, E] f32, expert weights [E, D, n_out] bf16
+    bits and a dense weight [D, D] bf16 bits, all ~N(0, sigma)."""
+    x = _act_encode(_normal(seed, TID_X, 0, T * D, x_sigma).reshape(T, D), BF16)
+    W_r = _normal(seed, TID_WR, 0, D * E, wr_sigma).reshape(D, E)
+    W_lin = np.stack([_act_encode(_normal(seed, TID_WD, e, D * n_out, w_sigma).reshape(D, n_out), BF16)
+                      for e in range(E)])
+    W_dense = _act_encode(_normal(seed, TID_WG, 0, D * D, w_sigma).reshape(D, D), BF16)
+    return x, W_r, W_lin, W_dense
+
+
 def make_inputs(cfg: Config, seed: int = 0, with_experts: bool = True) -> Inputs:
     x = _act_encode(_normal(seed, TID_X, 0, cfg.T * cfg.D, cfg.x_sigma).reshape(cfg.T, cfg.D), cfg.act)
     W_r = _normal(seed, TID_WR, 0, cfg.D * cfg.E, cfg.wr_sigma).reshape(cfg.D, cfg.E)
