@@ -17,14 +17,13 @@ calls and the buffers).
 * Top-k sweep ("DeepSeek-V4.1-Flash fine-grained MoE (5A)", sec. 4,
   profiling: per-token time at top-k 1, 2, 4 for the same sequence length,
   with percentiles, and a record that checks the shared expert is not added
-  twice); the sweep itself is bench.py --study topk. Reading: per-token time is step time / T over repeated steps
-  (p50/p95/p99 over steps); the "top misses" are the (token, slot) pairs
-  that the dispatch did not keep; the shared-expert check compares
-  y(with shared) - y(without shared) with the shared expert's own output.
+  twice); the sweep itself is bench.py --study topk. Reading: per-token
+  time is step time / T over repeated steps (p50/p95/p99 over steps); the
+  "top misses" are the (token, slot) pairs that the dispatch did not keep;
+  the shared-expert check compares y(with shared) - y(without shared) with
+  the shared expert's own output.
 """
 from __future__ import annotations
-
-import ctypes
 
 import torch
 
