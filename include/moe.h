@@ -122,8 +122,8 @@ typedef struct moe_weights {
  * MOE_WS_EXPERT_FFN for moe_expert_ffn / _gate_up / _down (the device tile
  * map and, with bf16 weights, 64 MiB of fp32 partial sums plus ready flags
  * for the GEMM tiles that are split along K), MOE_WS_FORWARD for
- * moe_forward (all of the above plus x_perm, H, y_perm and, with a shared
- * expert, its H and output). A workspace carries state only within one
+ * moe_forward (all of the above plus H, y_perm, x_perm for fp32
+ * activations only, and, with a shared expert, its H and output). A workspace carries state only within one
  * call; calls that run concurrently need separate workspaces. */
 int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes);
 
@@ -185,7 +185,10 @@ int moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot_pos
 /* The whole layer: route, dispatch, routed experts, shared expert (when
  * cfg->shared_F > 0) and combine, enqueued back to back with no host
  * synchronisation. topk_idx, topk_w, counts and offsets are optional
- * outputs (NULL: kept in the workspace). */
+ * outputs (NULL: kept in the workspace). With bf16 activations the gate/up
+ * GEMM fetches each routed row from x through perm_token, so the
+ * dispatched copy x_perm is never written; the results are the same as
+ * those of the stage entry points. */
 int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
                 const moe_weights* w, void* y, int32_t* topk_idx, float* topk_w,
                 int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream);

@@ -119,7 +119,8 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   f.perm = static_cast<int32_t*>(cv.take(tk * 4));
   f.chunk_ws = static_cast<int32_t*>(cv.take(dispatch_ws(c)));
   f.tilemap = static_cast<int32_t*>(cv.take(ffn_ws(c)));
-  f.x_perm = cv.take(tk * c.D * act_size(c));
+  // bf16: gate/up gathers its rows from x through perm (no dispatched copy)
+  f.x_perm = c.act_dtype == MOE_F32 ? cv.take(tk * c.D * act_size(c)) : nullptr;
   f.H = cv.take(tk * c.F * act_size(c));
   f.y_perm = static_cast<float*>(cv.take(tk * c.D * 4));
   f.H_shared = c.shared_F > 0 ? cv.take((size_t)c.T * c.shared_F * 2) : nullptr;
@@ -143,8 +144,11 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
 }
 
 // gate + up with the SwiGLU epilogue -> H
-hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
-                       const moe_weights& w, void* H, int32_t* tilemap, hipStream_t s) {
+// (gather: nullptr, x_perm holds the dispatched rows; else x_perm is x and
+// routed row r reads row gather[r] of it)
+hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gather,
+                       const int32_t* offsets, const moe_weights& w, void* H, int32_t* tilemap,
+                       hipStream_t s) {
   if (c.act_dtype == MOE_F32)
     return moe::launch_ffn_f32_gate_up(c, static_cast<const float*>(x_perm), offsets,
                                        static_cast<const float*>(w.W_gate),
@@ -153,6 +157,8 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* offs
   if (e != hipSuccess) return e;
   moe::GemmProblem g = routed_problem(c, offsets, tilemap);
   g.A = x_perm;
+  g.gather = gather;
+  g.gather_rows = c.T;
   g.K = c.D;
   g.N = c.F;
   g.B0 = w.W_gate;
@@ -184,10 +190,10 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
   return moe::launch_gemm_down(g, s);
 }
 
-hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
-                          const moe_weights& w, void* H, float* y_perm, int32_t* tilemap,
-                          hipStream_t s) {
-  hipError_t e = run_gate_up(c, x_perm, offsets, w, H, tilemap, s);
+hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* gather,
+                          const int32_t* offsets, const moe_weights& w, void* H, float* y_perm,
+                          int32_t* tilemap, hipStream_t s) {
+  hipError_t e = run_gate_up(c, x_perm, gather, offsets, w, H, tilemap, s);
   if (e != hipSuccess) return e;
   return run_down(c, H, offsets, w, y_perm, tilemap, false, s);
 }
@@ -288,7 +294,7 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offset
   if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
-  return hip_status(run_expert_ffn(*cfg, x_perm, offsets, *w, H, y_perm,
+  return hip_status(run_expert_ffn(*cfg, x_perm, nullptr, offsets, *w, H, y_perm,
                                    static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
 }
 
@@ -301,7 +307,7 @@ int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* of
   if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
-  return hip_status(run_gate_up(*cfg, x_perm, offsets, *w, H, static_cast<int32_t*>(ws),
+  return hip_status(run_gate_up(*cfg, x_perm, nullptr, offsets, *w, H, static_cast<int32_t*>(ws),
                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -363,7 +369,12 @@ int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float
   hipError_t e = moe::launch_router(c, x, W_r, bias, idx, tw, nullptr, s);
   if (e == hipSuccess)
     e = moe::launch_dispatch(c, idx, x, cnt, off, f.slot_pos, f.perm, f.x_perm, f.chunk_ws, s);
-  if (e == hipSuccess) e = run_expert_ffn(c, f.x_perm, off, *w, f.H, f.y_perm, f.tilemap, s);
+  if (e == hipSuccess) {
+    if (f.x_perm)  // fp32 activations: the VALU path reads dispatched rows
+      e = run_expert_ffn(c, f.x_perm, nullptr, off, *w, f.H, f.y_perm, f.tilemap, s);
+    else
+      e = run_expert_ffn(c, x, f.perm, off, *w, f.H, f.y_perm, f.tilemap, s);
+  }
   if (e == hipSuccess && c.shared_F > 0) e = run_shared(c, x, *w, f.H_shared, f.y_shared, s);
   if (e == hipSuccess) e = moe::launch_combine(c, f.y_perm, f.slot_pos, tw, f.y_shared, y, s);
   return hip_status(e);

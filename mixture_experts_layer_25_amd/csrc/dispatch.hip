@@ -205,6 +205,7 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
   dispatch_scan_kernel<<<ceil_div(c.E, 4), 256, 0, s>>>(c.E, nchunks, chunk_ws, counts);
   dispatch_rank_kernel<<<nchunks, 256, 0, s>>>(idx, counts, chunk_ws, c.T, c.E, c.top_k,
                                                c.capacity, nchunks, offsets, slot_pos, perm);
+  if (!x_perm) return hipGetLastError();  // the caller gathers rows through perm
   const size_t row_bytes = (size_t)c.D * (c.act_dtype == MOE_BF16 ? 2 : 4);
   dispatch_copy_kernel<<<ceil_div(c.T, 4), 256, 0, s>>>(
       static_cast<const uint4*>(x), slot_pos, c.T, c.top_k, static_cast<int>(row_bytes / 16),

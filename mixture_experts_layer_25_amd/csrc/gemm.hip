@@ -25,6 +25,9 @@
 // one row (A) or one column (B).
 //   A (X rows, K-contiguous): copied as 16-byte pieces to LDS rows of 64
 //   bytes (4 k-groups, slot = k-group ^ swz4(row)), read with ds_read_b128.
+//   With a gather list (the fused layer passes perm_token), routed row r
+//   is copied from row gather[r] of x: each copy lane looks its two row
+//   addresses up once per tile, so the dispatched copy of x is never built.
 //   B bf16 ([K][N], N-contiguous): k-rows of 512 bytes (32 chunks of 8
 //   columns, slot = chunk ^ 4 (k mod 4)) stored untouched; the MFMA fragment
 //   is read with the gfx950 transposing LDS load ds_read_b64_tr_b16 (within
@@ -94,6 +97,8 @@ enum { MODE_SWIGLU = 0, MODE_DOWN = 1 };
 
 struct Args {
   const uint16_t* A;
+  const int32_t* gather;  // A row of tile row r: gather[r] (< gather_rows), or r when nullptr
+  int gather_rows;
   const int32_t* tilemap;
   const int32_t* offsets;
   int rows, max_tiles, K, N, n_tiles_n;
@@ -327,7 +332,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int p = 512 * r + tid, m = p >> 2, q = (p & 3) ^ swz4(m);
-    a_g[r] = a.A + (size_t)min(row0 + m, row_end - 1) * K + kt_begin * BK + 8 * q;
+    int arow = min(row0 + m, row_end - 1);
+    if (a.gather) arow = min((unsigned)a.gather[arow], (unsigned)(a.gather_rows - 1));
+    a_g[r] = a.A + (size_t)arow * K + kt_begin * BK + 8 * q;
   }
   // ---- B copies.
   //   bf16: LDS k-row (512 bytes = 32 chunks of 8 columns) slot c holds
@@ -793,6 +800,8 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   Args a;
   a.A = static_cast<const uint16_t*>(p.A);
+  a.gather = p.gather;
+  a.gather_rows = p.gather_rows;
   a.tilemap = p.tilemap;
   a.offsets = p.offsets;
   a.rows = p.rows;

@@ -53,7 +53,9 @@ hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* til
 // bf16 activations: grouped MFMA GEMMs over the tile map. A dense launch
 // (tilemap == nullptr) treats rows [0, rows) as one segment of expert 0.
 struct GemmProblem {
-  const void* A;           // [rows][K] bf16
+  const void* A;           // [rows][K] bf16, or [gather_rows][K] when gathered
+  const int32_t* gather;   // nullptr, or the A row of each routed row (perm_token)
+  int gather_rows;
   const int32_t* tilemap;  // nullptr: dense
   const int32_t* offsets;  // segment ends (offsets[e+1]); unused when dense
   int rows;                // dense row count / grid bound
