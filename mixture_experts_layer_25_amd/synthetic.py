@@ -36,7 +36,13 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # dtype and gating codes; they mirror the C header's enums.
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, MXFP4_A8 = 0, 1, 2, 3
+# MXFP4_A8: the same MXFP4 weights; the routed experts' products take their
+# activation operands (x rows, H) as MXFP8 blocks.
+
+
+def is_mx(wdt: int) -> bool:
+    return wdt in (MXFP4, MXFP4_A8)
 GATE_SOFTMAX, GATE_SIGMOID, GATE_SQRT_SOFTPLUS = 0, 1, 2
 
 TID_X, TID_WR, TID_BIAS = 1, 2, 3
@@ -90,6 +96,10 @@ CONFIGS = {
                             renorm=0, clamp=10.0, shared_F=1024,
                             bias="normal", bias_sigma=0.1),
 }
+# The 384-expert layer with MXFP8 activation operands in the routed experts
+# (an opt-in mode of the same weights; not one of the five workloads above).
+CONFIGS["fine384_mxfp4_a8"] = CONFIGS["fine384_mxfp4"].replace(name="fine384_mxfp4_a8",
+                                                               wdt=MXFP4_A8)
 CONFIG_ORDER = ["tiny_fp32", "mixtral", "capacity", "fine128", "fine384_mxfp4"]
 
 
@@ -201,7 +211,7 @@ def make_expert_weights(cfg: Config, tid: int, K: int, N: int, seed: int = 0,
 
     def one(e):
         w = _normal(seed, tid, e, K * N, cfg.w_sigma).reshape(K, N)
-        if cfg.wdt == MXFP4:
+        if is_mx(cfg.wdt):
             codes, scales = quantize_mxfp4_rows(np.ascontiguousarray(w.T))
             return (np.ascontiguousarray(codes.reshape(N, K // 32, 16).transpose(1, 0, 2)),
                     np.ascontiguousarray(scales.T))
@@ -215,7 +225,7 @@ def make_expert_weights(cfg: Config, tid: int, K: int, N: int, seed: int = 0,
     finally:
         if own:
             pool.shutdown()
-    if cfg.wdt == MXFP4:
+    if is_mx(cfg.wdt):
         codes = np.stack([p[0] for p in parts])
         scales = np.stack([p[1] for p in parts])
         return codes, scales
@@ -242,7 +252,7 @@ def make_inputs(cfg: Config, seed: int = 0, with_experts: bool = True) -> Inputs
     if not with_experts:
         return inp
     with ThreadPoolExecutor(_threads()) as pool:
-        if cfg.wdt == MXFP4:
+        if is_mx(cfg.wdt):
             inp.W_gate, inp.S_gate = make_expert_weights(cfg, TID_WG, cfg.D, cfg.F, seed, pool)
             inp.W_up, inp.S_up = make_expert_weights(cfg, TID_WU, cfg.D, cfg.F, seed, pool)
             inp.W_down, inp.S_down = make_expert_weights(cfg, TID_WD, cfg.F, cfg.D, seed, pool)

@@ -14,6 +14,11 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   expert / shared pinned: E=1,k=1 SwiGLU against a numpy matmul chain,
                   clamp closed form, dense-masked brute force
   forward_tokens  pinned: dense all-experts masked brute force
+  e4m3 / e4m3_encode / mxfp8_quantize
+                  pinned: format values, exhaustive midpoints and ties,
+                  torch's float8_e4m3fn rounding, block exponent, saturation,
+                  round trips, error bound
+  MXFP4_A8 experts pinned: numpy chain over the pinned quantiser
 Full-size outputs are pinned only through the above (accumulation order,
 exp/log1p ulps and bf16 ties of H are covered by the tolerance).
 """
@@ -29,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 
-OR_F32, OR_BF16, OR_MXFP4 = 0, 1, 2
+OR_F32, OR_BF16, OR_MXFP4, OR_MXFP4_A8 = 0, 1, 2, 3
 OR_SOFTMAX, OR_SIGMOID, OR_SQRT_SOFTPLUS = 0, 1, 2
 
 
@@ -75,6 +80,11 @@ def lib():
         L.oracle_e2m1.argtypes = [ctypes.c_uint]
         L.oracle_e8m0.restype = ctypes.c_double
         L.oracle_e8m0.argtypes = [ctypes.c_uint]
+        L.oracle_e4m3.restype = ctypes.c_double
+        L.oracle_e4m3.argtypes = [ctypes.c_uint]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_mxfp8_quantize.argtypes = [vp, i32, vp, vp]
         L.oracle_softplus.restype = ctypes.c_double
         L.oracle_softplus.argtypes = [ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
@@ -126,6 +136,32 @@ def e2m1(code: int) -> float:
 
 def e8m0(s: int) -> float:
     return lib().oracle_e8m0(s)
+
+
+def e4m3(code: int) -> float:
+    return lib().oracle_e4m3(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().oracle_e4m3_encode(float(v))
+
+
+def mxfp8_quantize(v):
+    """MXFP8 codes (uint8, same shape) and scales (uint8, last axis / 32) of
+    float64 values whose last axis is a multiple of 32."""
+    v = np.ascontiguousarray(v, np.float64)
+    assert v.shape[-1] % 32 == 0
+    codes = np.empty(v.shape, np.uint8)
+    scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    lib().oracle_mxfp8_quantize(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp8_values(codes, scales):
+    """The values MXFP8 codes and scales represent (float64)."""
+    dec = np.array([e4m3(c) for c in range(256)])
+    sc = np.array([e8m0(s) if s < 255 else np.nan for s in range(256)])
+    return dec[codes] * np.repeat(sc[scales], 32, axis=-1)
 
 
 def softplus(s: float) -> float:

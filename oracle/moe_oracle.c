@@ -27,8 +27,11 @@
  *         (blogdee.com): sigmoid gating as the mixing-weight function.
  *  [ECHO] "moe f&b compute flow" (Echo's blog): the Router -> Dispatch ->
  *         FFN -> Combine stages; softmax makes weights positive, summing to 1.
- *  [OCP]  OCP Microscaling Formats (MX) v1.0: e2m1 element values and the
- *         e8m0 scale 2^(s-127) (the pages only say the experts are FP4).
+ *  [OCP]  OCP Microscaling Formats (MX) v1.0: e2m1 and e4m3 element values,
+ *         the e8m0 scale 2^(s-127) and the block conversion (shared
+ *         exponent from the block maximum); the pages only say the experts
+ *         are FP4, and the MXFP8 activation mode (OR_MXFP4_A8) is an
+ *         addition that lets the products run on the scaled MFMA.
  *
  * Readings where the pages leave a step open (each is listed with its reason
  * in the design notes):
@@ -95,6 +98,68 @@ double oracle_e2m1(unsigned code) {
 double oracle_e8m0(unsigned s) {
   if (s == 255u) return NAN;
   return ldexp(1.0, (int)s - 127);
+}
+
+/* e4m3 (the MX FP8 E4M3 element): bit 7 sign, bits 6..3 exponent (bias 7),
+ * bits 2..0 mantissa; exponent field 0 holds the subnormals m/8 * 2^-6;
+ * S.1111.111 is NaN and there is no infinity, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448 [OCP]. */
+double oracle_e4m3(unsigned code) {
+  unsigned e = (code >> 3) & 15u, m = code & 7u;
+  if (e == 15u && m == 7u) return NAN;
+  double v = e == 0u ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, (int)e - 7);
+  return (code & 0x80u) ? -v : v;
+}
+
+/* The e4m3 code nearest to v (finite), ties to the code whose last bit is
+ * 0, magnitudes beyond 448 saturated to 448. Written as a search over the
+ * 127 non-negative finite codes, which are increasing in value. */
+unsigned oracle_e4m3_encode(double v) {
+  const double a = fabs(v);
+  unsigned best = 0;
+  double best_d = a;
+  for (unsigned c = 1; c < 127u; ++c) {
+    const double d = fabs(oracle_e4m3(c) - a);
+    if (d < best_d || (d == best_d && (c & 1u) == 0u)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (signbit(v) ? 0x80u : 0u) | best;
+}
+
+/* MXFP8 quantisation of n values (n a multiple of 32), block by block of 32
+ * consecutive values [OCP, the MX conversion]: the block's shared exponent
+ * is floor(log2(max |V_i|)) minus 8 (the exponent of e4m3's largest
+ * normal), held in e8m0, so clamped to [-127, 127] (a block of zeros gets
+ * -127, scale code 0); X = 2^exponent; element i is the e4m3 code of
+ * V_i / X, rounded as oracle_e4m3_encode does. */
+void oracle_mxfp8_quantize(const double* v, int n, uint8_t* codes, uint8_t* scales) {
+  for (int b = 0; b < n / 32; ++b) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[32 * b + i]));
+    int ex = -127;
+    if (amax > 0.0) {
+      int e2;
+      frexp(amax, &e2);  /* amax = m 2^e2, 0.5 <= m < 1: floor(log2 amax) = e2 - 1 */
+      ex = e2 - 1 - 8;
+      if (ex < -127) ex = -127;
+      if (ex > 127) ex = 127;
+    }
+    scales[b] = (uint8_t)(ex + 127);
+    for (int i = 0; i < 32; ++i)
+      codes[32 * b + i] = (uint8_t)oracle_e4m3_encode(ldexp(v[32 * b + i], -ex));
+  }
+}
+
+/* v <- the values its MXFP8 quantisation represents. */
+static void mxfp8_round_trip(double* v, int n) {
+  uint8_t* codes = (uint8_t*)malloc((size_t)n);
+  uint8_t* scales = (uint8_t*)malloc((size_t)n / 32);
+  oracle_mxfp8_quantize(v, n, codes, scales);
+  for (int i = 0; i < n; ++i) v[i] = oracle_e4m3(codes[i]) * oracle_e8m0(scales[i / 32]);
+  free(codes);
+  free(scales);
 }
 
 /* softplus(s) = log(1 + e^s), written in the form that cannot overflow:
@@ -278,12 +343,18 @@ void oracle_dispatch(const oracle_cfg* c, const int32_t* topk_idx, int32_t* coun
  *   g = x W_gate, u = x W_up (clamped to [-L, L] when L > 0 [DSV sec. 1, 3]),
  *   h = SiLU(g) * u, rounded to bf16 when the activations are bf16,
  *   o = h W_down.
+ * With OR_MXFP4_A8 weights, x and h are replaced by their MXFP8 values
+ * (oracle_mxfp8_quantize) before the products that read them.
  * h_out [nrows][F] and o_out [nrows][D] may be NULL. */
 static void swiglu_rows(const oracle_cfg* c, int F, const void* Wg, const void* Wu, const void* Wd,
                         const uint8_t* Sg, const uint8_t* Su, const uint8_t* Sd,
                         const oracle_cfg* wc, int e, int nrows, const void* x,
                         const int32_t* rows, double* h_out, double* o_out) {
   const int D = c->D;
+  /* MXFP4 weights with MXFP8 activation operands: the x row and H enter
+   * the products as their MXFP8 values (H quantised from its fp32 value,
+   * the precision in which the GPU forms it). */
+  const int a8 = wc->wdt == OR_MXFP4_A8;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int r = 0; r < nrows; ++r) {
     double* xr = (double*)malloc(sizeof(double) * (size_t)D);
@@ -291,6 +362,7 @@ static void swiglu_rows(const oracle_cfg* c, int F, const void* Wg, const void* 
     double* u = (double*)calloc((size_t)F, sizeof(double));
     double* h = (double*)malloc(sizeof(double) * (size_t)F);
     for (int d = 0; d < D; ++d) xr[d] = act_f32(c, x, (size_t)rows[r] * D + d);
+    if (a8) mxfp8_round_trip(xr, D);
     for (int d = 0; d < D; ++d) {
       for (int f = 0; f < F; ++f) {
         g[f] += xr[d] * wt(wc, Wg, Sg, e, D, F, d, f);
@@ -305,10 +377,13 @@ static void swiglu_rows(const oracle_cfg* c, int F, const void* Wg, const void* 
         uf = fmin(fmax(uf, -L), L);
       }
       double hv = oracle_silu(gf) * uf;
-      if (c->act == OR_BF16) hv = oracle_bf16_to_double(oracle_double_to_bf16(hv));
+      if (a8) hv = (double)(float)hv;  /* quantised below from its fp32 value */
+      else if (c->act == OR_BF16) hv = oracle_bf16_to_double(oracle_double_to_bf16(hv));
       h[f] = hv;
-      if (h_out) h_out[(size_t)r * F + f] = hv;
     }
+    if (a8) mxfp8_round_trip(h, F);
+    if (h_out)
+      for (int f = 0; f < F; ++f) h_out[(size_t)r * F + f] = h[f];
     if (o_out) {
       double* o = o_out + (size_t)r * D;
       for (int cc = 0; cc < D; ++cc) o[cc] = 0.0;

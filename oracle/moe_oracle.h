@@ -8,7 +8,8 @@
  *
  * Precision: the router is fp32 (the pages fix it); everything after the
  * router is computed in double and rounded once where the layer's contract
- * says a value is stored in a narrower type (H and y in bf16).
+ * says a value is stored in a narrower type (H and y in bf16; x and H in
+ * MXFP8 for OR_MXFP4_A8 weights).
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -18,7 +19,9 @@
 extern "C" {
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2 };
+/* OR_MXFP4_A8: MXFP4 weights whose products take the activation operands
+ * (the x rows and H of the routed experts) as MXFP8 e4m3 blocks. */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2, OR_MXFP4_A8 = 3 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1, OR_SQRT_SOFTPLUS = 2 };
 
 typedef struct {
@@ -28,7 +31,7 @@ typedef struct {
   int32_t capacity;   /* <= 0: unlimited */
   float clamp;        /* <= 0: none; else gate and up clamped to [-clamp, clamp] */
   int32_t act;        /* OR_F32 or OR_BF16 */
-  int32_t wdt;        /* OR_F32, OR_BF16 or OR_MXFP4 */
+  int32_t wdt;        /* OR_F32, OR_BF16, OR_MXFP4 or OR_MXFP4_A8 */
   int32_t shared_F;   /* 0: no shared expert */
 } oracle_cfg;
 
@@ -42,6 +45,9 @@ double oracle_bf16_to_double(uint16_t b);
 uint16_t oracle_double_to_bf16(double v);
 double oracle_e2m1(unsigned code);
 double oracle_e8m0(unsigned s);
+double oracle_e4m3(unsigned code);
+unsigned oracle_e4m3_encode(double v);
+void oracle_mxfp8_quantize(const double* v, int n, uint8_t* codes, uint8_t* scales);
 double oracle_softplus(double s);
 double oracle_silu(double z);
 int oracle_capacity_formula(int S, int top_k, int num_experts);
