@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s (1 GPU) + grouped-GEMM TFLOP/s as % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
@@ -84,6 +85,9 @@ def roofline_kernel(cfg):
     file and what bounds it."""
     if cfg.wdt == 0:
         return {"name": "ffn_f32_gateup_kernel", "src": "ffn_f32.hip", "bound": "alu"}
+    if cfg.wdt == 3:  # e4m3 x e2m1 products run at the fp8 MFMA rate
+        return {"name": "gemm_a8_kernel<0>", "src": "gemm_a8.hip", "bound": "mfma",
+                "peak": PEAK_FP8_TFLOPS}
     if cfg.wdt == 2:
         return {"name": "gemm_kernel<0, true>", "src": "gemm.hip", "bound": "mfma"}
     return {"name": "gemm_kernel<0, false>", "src": "gemm.hip", "bound": "mfma"}
@@ -483,7 +487,7 @@ def main():
     if rk["bound"] == "alu":
         peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
     else:
-        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+        peak, unit = rk.get("peak", PEAK_BF16_TFLOPS), "TFLOP/s"
     roofline = {"bound": rk["bound"], "achieved": gu_tf, "peak": peak, "unit": unit,
                 "frac": gu_tf / peak, "traffic": traffic,
                 "kernel": rk["name"],
@@ -508,11 +512,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.act == 1 else "f32",
+        "dtype": ("mxfp8" if cfg.wdt == 3 else "bf16") if cfg.act == 1 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} D={cfg.D} E={E} top-{k} F={cfg.F} "
                                f"{'bf16' if cfg.act == 1 else 'fp32'} act, "
-                               f"{['fp32', 'bf16', 'mxfp4'][cfg.wdt]} weights",
+                               f"{['fp32', 'bf16', 'mxfp4', 'mxfp4'][cfg.wdt]} weights"
+                               f"{', mxfp8 expert activations' if cfg.wdt == 3 else ''}",
                    "tokens": T, "kept_pairs": A, "seed": 0},
         "grouped_gemm_tflops": gemm_tf,
         "grouped_gemm_frac_of_bf16_peak": gemm_tf / PEAK_BF16_TFLOPS,

@@ -41,6 +41,8 @@
  *   slot_pos int32 [T][k]   row of (t, j) in the segments, -1 if dropped
  *   perm_token int32 [T*k]  token of each segment row (rows < A written)
  *   x_perm   [T*k][D] act dtype  H [T*k][F] act dtype  y_perm [T*k][D] fp32
+ *   (MOE_MXFP4_A8: H holds MXFP8, e4m3 codes uint8 [T*k][F] followed by
+ *   e8m0 scales uint8 [T*k][F/32], in the same [T*k][F] bf16-sized buffer)
  *   y        [T][D]   act dtype
  * Every device pointer must be 16-byte aligned.
  *
@@ -59,9 +61,17 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+/* MOE_MXFP4_A8: the MXFP4 weights of MOE_MXFP4 (same layout), with the
+ * routed experts' activation operands (the x rows and H) quantised to
+ * MXFP8 (OCP MX v1.0: e4m3 elements, one e8m0 scale per 32 values along
+ * K) so that the products run on the block-scaled MFMA. The pages store the
+ * routed experts in FP4 and say nothing of the activations; this mode is an
+ * opt-in addition. The quantisation of a block of 32 values v: exponent
+ * X = floor(log2 max|v|) - 8, clamped to [-127, 127] (-127 for a zero
+ * block); element = e4m3 of v / 2^X, ties to even, saturated at +-448. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_MXFP4_A8 = 3 } moe_dtype;
 
 typedef enum {
   MOE_GATE_SOFTMAX = 0,       /* p = softmax(logit + bias) over all E */
@@ -95,7 +105,8 @@ typedef enum {
  *             [-clamp, clamp] before SiLU(gate)*up ("DeepSeek-V4.1-Flash"
  *             sec. 1, 3), in routed and shared experts.
  *   act_dtype MOE_F32 (then w_dtype MOE_F32) or MOE_BF16 (then w_dtype
- *             MOE_BF16 or MOE_MXFP4).
+ *             MOE_BF16, MOE_MXFP4 or MOE_MXFP4_A8; MOE_MXFP4_A8 needs D
+ *             and F multiples of 64).
  *   shared_F  0: no shared expert; else the width of one always-on bf16
  *             SwiGLU expert added with weight 1 (requires MOE_BF16). */
 typedef struct moe_cfg {
@@ -120,11 +131,13 @@ typedef struct moe_weights {
 /* Bytes of workspace a call needs (host out-parameter `bytes`).
  * MOE_WS_DISPATCH for moe_dispatch (per-chunk expert counts),
  * MOE_WS_EXPERT_FFN for moe_expert_ffn / _gate_up / _down (the device tile
- * map and, with bf16 weights, 64 MiB of fp32 partial sums plus ready flags
- * for the GEMM tiles that are split along K), MOE_WS_FORWARD for
+ * map and, with bf16 activations, 64 MiB of fp32 partial sums plus ready
+ * flags for the GEMM tiles that are split along K; with MOE_MXFP4_A8 also
+ * the MXFP8 copy of x_perm), MOE_WS_FORWARD for
  * moe_forward (all of the above plus H, y_perm, x_perm for fp32
- * activations only, and, with a shared expert, its H and output). A workspace carries state only within one
- * call; calls that run concurrently need separate workspaces. */
+ * activations only, the MXFP8 copy of x for MOE_MXFP4_A8 and, with a
+ * shared expert, its H and output). A workspace carries state only within
+ * one call; calls that run concurrently need separate workspaces. */
 int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes);
 
 /* Router ("FFN, SwiGLU and MoE" sec. 3; "ops-transformer" MoEForward steps
@@ -155,6 +168,8 @@ int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int
  * for every kept row r of expert e's segment,
  *   H[r] = SiLU(clampL(x_perm[r] W_gate[e])) * clampL(x_perm[r] W_up[e])
  *          (rounded to the act dtype), y_perm[r] = H[r] W_down[e] (fp32).
+ * With MOE_MXFP4_A8 the products read the MXFP8 values of x_perm[r] and of
+ * H[r] (H computed in fp32, then stored as MXFP8).
  * Rows r >= offsets[E] are not written. */
 int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
                    const moe_weights* w, void* H, float* y_perm, void* ws, size_t ws_bytes,
@@ -192,6 +207,14 @@ int moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot_pos
 int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
                 const moe_weights* w, void* y, int32_t* topk_idx, float* topk_w,
                 int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream);
+
+/* MXFP8 quantisation of bf16 rows, the activation format of MOE_MXFP4_A8
+ * (OCP MX v1.0 conversion, as stated at MOE_MXFP4_A8): x [rows][K] bf16 ->
+ * e4m3 codes uint8 [rows][K] and e8m0 scales uint8 [rows][K/32], one scale
+ * per 32 consecutive values of a row. K must be a positive multiple of 32
+ * and rows >= 0; inputs are expected to be finite. */
+int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream);
 
 /* Static text for a moe_status value (host pointer, never NULL). */
 const char* moe_status_string(int status);

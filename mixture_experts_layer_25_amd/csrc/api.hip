@@ -20,6 +20,8 @@ bool dev_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
 
 size_t act_size(const moe_cfg& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
+bool is_a8(const moe_cfg& c) { return c.w_dtype == MOE_MXFP4_A8; }
+bool is_mx(const moe_cfg& c) { return c.w_dtype == MOE_MXFP4 || is_a8(c); }
 
 int check_cfg(const moe_cfg* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
@@ -31,13 +33,15 @@ int check_cfg(const moe_cfg* c) {
   if (isnan(c->clamp) || isinf(c->clamp)) return MOE_ERR_INVALID_ARG;
   if (c->shared_F < 0) return MOE_ERR_INVALID_ARG;
   const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32;
-  const bool bf = c->act_dtype == MOE_BF16 && (c->w_dtype == MOE_BF16 || c->w_dtype == MOE_MXFP4);
+  const bool bf = c->act_dtype == MOE_BF16 &&
+                  (c->w_dtype == MOE_BF16 || c->w_dtype == MOE_MXFP4 || c->w_dtype == MOE_MXFP4_A8);
   if (!f32 && !bf) return MOE_ERR_INVALID_ARG;
   if (c->E > kMaxE || c->top_k > kMaxK) return MOE_ERR_UNSUPPORTED;
   // row and element indices are int32 on the device side
   if ((long long)c->T * c->top_k > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
   if (bf) {
     if (c->D % 32 || c->F % 32) return MOE_ERR_UNSUPPORTED;  // GEMM K steps of 32
+    if (is_a8(*c) && (c->D % 64 || c->F % 64)) return MOE_ERR_UNSUPPORTED;  // and of 64
   } else {
     if (c->D > 16384 || c->F > 16384) return MOE_ERR_UNSUPPORTED;
   }
@@ -51,7 +55,7 @@ int check_cfg(const moe_cfg* c) {
 int check_weights(const moe_cfg& c, const moe_weights* w) {
   if (!w) return MOE_ERR_INVALID_ARG;
   if (!dev_ok(w->W_gate) || !dev_ok(w->W_up) || !dev_ok(w->W_down)) return MOE_ERR_INVALID_ARG;
-  if (c.w_dtype == MOE_MXFP4) {
+  if (is_mx(c)) {
     if (!w->S_gate || !w->S_up || !w->S_down) return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
@@ -90,6 +94,18 @@ size_t dispatch_ws(const moe_cfg& c) {
 // partial-sum slots of the grouped GEMMs
 size_t tilemap_bytes(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
 size_t ffn_ws(const moe_cfg& c) { return tilemap_bytes(c) + moe::split_bytes(c); }
+// MXFP8 copy of `rows` activation rows of width K: codes, then scales
+size_t mxfp8_bytes(size_t rows, int K) {
+  return moe::align_up(rows * K, kAlign) + moe::align_up(rows * (K / 32), kAlign);
+}
+// the stage entry points' FFN workspace: with MXFP8 activations, the
+// quantised x_perm follows the tile map and split slots
+size_t ffn_stage_ws(const moe_cfg& c) {
+  return ffn_ws(c) + (is_a8(c) ? mxfp8_bytes((size_t)c.T * c.top_k, c.D) : 0);
+}
+uint8_t* stage_xq(const moe_cfg& c, void* ws) {
+  return is_a8(c) ? static_cast<uint8_t*>(ws) + ffn_ws(c) : nullptr;
+}
 int32_t* split_flags_of(const moe_cfg& c, int32_t* tilemap) {
   if (!moe::gemm_splits(c)) return nullptr;
   return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tilemap) + tilemap_bytes(c));
@@ -104,6 +120,7 @@ struct ForwardWs {
   int32_t *idx, *counts, *offsets, *slot_pos, *perm, *chunk_ws, *tilemap;
   float *w, *y_perm, *y_shared;
   void *x_perm, *H, *H_shared;
+  uint8_t* xq;  // MXFP8 copy of x (MXFP8 activations)
   size_t bytes;
 };
 
@@ -121,6 +138,7 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   f.tilemap = static_cast<int32_t*>(cv.take(ffn_ws(c)));
   // bf16: gate/up gathers its rows from x through perm (no dispatched copy)
   f.x_perm = c.act_dtype == MOE_F32 ? cv.take(tk * c.D * act_size(c)) : nullptr;
+  f.xq = is_a8(c) ? static_cast<uint8_t*>(cv.take(mxfp8_bytes(c.T, c.D))) : nullptr;
   f.H = cv.take(tk * c.F * act_size(c));
   f.y_perm = static_cast<float*>(cv.take(tk * c.D * 4));
   f.H_shared = c.shared_F > 0 ? cv.take((size_t)c.T * c.shared_F * 2) : nullptr;
@@ -136,7 +154,7 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
   g.rows = c.T * c.top_k;
   g.max_tiles = moe::max_mtiles(c);
   g.E = c.E;
-  g.mxfp4 = c.w_dtype == MOE_MXFP4;
+  g.mxfp4 = is_mx(c);
   g.clamp = c.clamp;
   g.split_flags = split_flags_of(c, tilemap);
   g.split_ws = split_ws_of(c, tilemap);
@@ -145,10 +163,12 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
 
 // gate + up with the SwiGLU epilogue -> H
 // (gather: nullptr, x_perm holds the dispatched rows; else x_perm is x and
-// routed row r reads row gather[r] of it)
+// routed row r reads row gather[r] of it). With MXFP8 activations the A
+// rows are first quantised into xq (codes, then scales) and H is written
+// as MXFP8 (codes [T*k][F], then scales [T*k][F/32]).
 hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gather,
                        const int32_t* offsets, const moe_weights& w, void* H, int32_t* tilemap,
-                       hipStream_t s) {
+                       uint8_t* xq, hipStream_t s) {
   if (c.act_dtype == MOE_F32)
     return moe::launch_ffn_f32_gate_up(c, static_cast<const float*>(x_perm), offsets,
                                        static_cast<const float*>(w.W_gate),
@@ -166,7 +186,14 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gath
   g.S0 = w.S_gate;
   g.S1 = w.S_up;
   g.out = H;
-  return moe::launch_gemm_swiglu(g, s);
+  if (!is_a8(c)) return moe::launch_gemm_swiglu(g, s);
+  const long long qrows = gather ? c.T : (long long)c.T * c.top_k;
+  uint8_t* xs = xq + moe::align_up((size_t)qrows * c.D, kAlign);
+  e = moe::launch_quant_mxfp8(x_perm, qrows, c.D, xq, xs, s);
+  if (e != hipSuccess) return e;
+  g.A = xq;
+  g.SA = xs;
+  return moe::launch_gemm_a8(g, true, s);
 }
 
 // down projection -> y_perm; rebuild_map = false reuses the tile map that a
@@ -187,13 +214,15 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
   g.B0 = w.W_down;
   g.S0 = w.S_down;
   g.out = y_perm;
-  return moe::launch_gemm_down(g, s);
+  if (!is_a8(c)) return moe::launch_gemm_down(g, s);
+  g.SA = static_cast<const uint8_t*>(H) + (size_t)g.rows * c.F;  // MXFP8 H: scales after codes
+  return moe::launch_gemm_a8(g, false, s);
 }
 
 hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* gather,
                           const int32_t* offsets, const moe_weights& w, void* H, float* y_perm,
-                          int32_t* tilemap, hipStream_t s) {
-  hipError_t e = run_gate_up(c, x_perm, gather, offsets, w, H, tilemap, s);
+                          int32_t* tilemap, uint8_t* xq, hipStream_t s) {
+  hipError_t e = run_gate_up(c, x_perm, gather, offsets, w, H, tilemap, xq, s);
   if (e != hipSuccess) return e;
   return run_down(c, H, offsets, w, y_perm, tilemap, false, s);
 }
@@ -250,7 +279,7 @@ int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes) {
   if (!bytes) return MOE_ERR_INVALID_ARG;
   switch (kind) {
     case MOE_WS_DISPATCH: *bytes = dispatch_ws(*cfg); return MOE_OK;
-    case MOE_WS_EXPERT_FFN: *bytes = cfg->act_dtype == MOE_F32 ? 0 : ffn_ws(*cfg); return MOE_OK;
+    case MOE_WS_EXPERT_FFN: *bytes = cfg->act_dtype == MOE_F32 ? 0 : ffn_stage_ws(*cfg); return MOE_OK;
     case MOE_WS_FORWARD: *bytes = carve_forward(*cfg, nullptr).bytes; return MOE_OK;
     default: return MOE_ERR_INVALID_ARG;
   }
@@ -291,11 +320,12 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offset
   if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
   if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(H) || !dev_ok(y_perm))
     return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_stage_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_expert_ffn(*cfg, x_perm, nullptr, offsets, *w, H, y_perm,
-                                   static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
+                                   static_cast<int32_t*>(ws), stage_xq(*cfg, ws),
+                                   static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
@@ -304,11 +334,11 @@ int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* of
   if (st != MOE_OK) return st;
   if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
   if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(H)) return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_stage_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_gate_up(*cfg, x_perm, nullptr, offsets, *w, H, static_cast<int32_t*>(ws),
-                                static_cast<hipStream_t>(stream)));
+                                stage_xq(*cfg, ws), static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
@@ -317,7 +347,7 @@ int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
   if (st != MOE_OK) return st;
   if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
   if (!dev_ok(H) || !dev_ok(offsets) || !dev_ok(y_perm)) return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_stage_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_down(*cfg, H, offsets, *w, y_perm, static_cast<int32_t*>(ws), true,
@@ -346,6 +376,15 @@ int moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot_pos
                                         static_cast<hipStream_t>(stream)));
 }
 
+int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (!dev_ok(x) || !dev_ok(codes) || !dev_ok(scales)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  return hip_status(moe::launch_quant_mxfp8(x, rows, K, codes, scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
                 const moe_weights* w, void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
                 int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
@@ -371,9 +410,9 @@ int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float
     e = moe::launch_dispatch(c, idx, x, cnt, off, f.slot_pos, f.perm, f.x_perm, f.chunk_ws, s);
   if (e == hipSuccess) {
     if (f.x_perm)  // fp32 activations: the VALU path reads dispatched rows
-      e = run_expert_ffn(c, f.x_perm, nullptr, off, *w, f.H, f.y_perm, f.tilemap, s);
+      e = run_expert_ffn(c, f.x_perm, nullptr, off, *w, f.H, f.y_perm, f.tilemap, nullptr, s);
     else
-      e = run_expert_ffn(c, x, f.perm, off, *w, f.H, f.y_perm, f.tilemap, s);
+      e = run_expert_ffn(c, x, f.perm, off, *w, f.H, f.y_perm, f.tilemap, f.xq, s);
   }
   if (e == hipSuccess && c.shared_F > 0) e = run_shared(c, x, *w, f.H_shared, f.y_shared, s);
   if (e == hipSuccess) e = moe::launch_combine(c, f.y_perm, f.slot_pos, tw, f.y_shared, y, s);

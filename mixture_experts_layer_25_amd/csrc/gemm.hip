@@ -65,8 +65,7 @@
 // tiles; the tiles of the last, partial round are split along K so that
 // the last round keeps every CU busy, their fp32 partial sums meeting in a
 // workspace in a fixed order.
-#include "common.h"
-#include "launch.h"
+#include "gemm_tile.h"
 
 // The asm blocks that issue LDS copies set M0 themselves and list it as
 // clobbered; clang warns about clobbering a reserved register.
@@ -76,14 +75,10 @@ namespace moe {
 namespace {
 
 constexpr int BK = 32;                  // k per step
-constexpr int TM = kBM;                 // 256 rows per tile
-constexpr int TN = 256;                 // B-columns per tile
 constexpr int A_BYTES = TM * BK * 2;    // 16 KB of A per step
 constexpr int B_BYTES = TN * BK * 2;    // 16 KB of bf16 B per step
 constexpr int MXC_BYTES = TN * 16;      // 4 KB of MXFP4 codes per step
 constexpr int MXS_BYTES = TN * 4;       // 1 KB of scales (one dword each) per step
-constexpr int kCUsPerXCD = 32;          // MI355X: 256 CUs in 8 XCDs
-constexpr int kMaxSplit = 8;            // K-parts of a split tile
 
 template <bool MX>
 struct Stages {
@@ -92,30 +87,6 @@ struct Stages {
   static constexpr int per = MX ? 3 : 4;    // copies per thread per step
   static_assert(count >= 4, "a barrier every two steps needs four stages");
 };
-
-enum { MODE_SWIGLU = 0, MODE_DOWN = 1 };
-
-struct Args {
-  const uint16_t* A;
-  const int32_t* gather;  // A row of tile row r: gather[r] (< gather_rows), or r when nullptr
-  int gather_rows;
-  const int32_t* tilemap;
-  const int32_t* offsets;
-  int rows, max_tiles, K, N, n_tiles_n;
-  const void* B0;
-  const void* B1;
-  const uint8_t* S0;
-  const uint8_t* S1;
-  float clamp;
-  void* out;
-  float* split_ws;       // partial accumulators of split tiles, or nullptr
-  int32_t* split_flags;  // one ready flag per partial slot, zero between launches
-};
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // e2m1 code -> binary32 bits (OCP MX v1.0: bit 3 sign, 2 exponent bits with
 // bias 1, 1 mantissa bit; exponent 0 encodes 0 and 0.5).
@@ -176,121 +147,12 @@ __device__ __forceinline__ void mx_fragments(uint32_t c0, uint32_t s0, uint32_t 
   f1 = __builtin_bit_cast(bf16x8_t, o1);
 }
 
-// Slot permutation of the 4 k-groups of a 64-byte A row: rows r..r+15 then
-// put any one k-group in 16 distinct 16-byte bank groups, and so do rows
-// r..r+3 with all 4 k-groups.
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
-}
-// Asynchronous copies global -> LDS: lane l's 16 bytes land at
-// lds_base + 16 l (dma16); lane l's byte lands, zero-extended to a dword,
-// at lds_base + 4 l (dma1).
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma1(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 1, 0, 0);
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// wait until at most `groups` steps of this thread's copies are in flight
-template <int PER>
-__device__ __forceinline__ void wait_copy_groups(int groups) {
-  switch (groups) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<PER>(); break;
-    case 2: wait_vmcnt<2 * PER>(); break;
-    case 3: wait_vmcnt<3 * PER>(); break;
-    case 4: wait_vmcnt<4 * PER>(); break;
-    case 5: wait_vmcnt<5 * PER>(); break;
-    default: wait_vmcnt<6 * PER>(); break;
-  }
-}
 
 // Wait states after an asm block's last MFMA so that whatever the compiler
 // places next (a register move, a spill, a VALU read) sees the finished
 // accumulator: the compiler does not look inside asm for MFMA hazards.
 #define MFMA_TAIL "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
 
-// Tile order, by expert: an expert's tiles are contiguous, in groups of up
-// to 8 of its M-tiles; inside a group N-tile major and M-tile minor. The 32
-// workgroups an XCD runs at once then cover about 8 M-tiles x 4 N-tiles of
-// one expert, so each weight slab is fetched once and shared by all those
-// M-tiles, and each activation slab by 4 N-tiles. With a tile map, M-tile
-// t / NT and the tile's own belong to the same expert (an expert's tiles
-// span whole rows of NT), which gives the expert's first M-tile and count
-// without a search.
-__device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int32_t* tilemap,
-                                               const int32_t* offsets, int& mt, int& nt) {
-  constexpr int MG = 8;
-  int first = 0, m = MT;
-  if (tilemap) {
-    const int g = t / NT;
-    const int e = tilemap[1 + 2 * g];
-    const int seg = offsets[e];
-    first = g - (tilemap[2 + 2 * g] - seg) / TM;
-    m = (offsets[e + 1] - seg + TM - 1) / TM;
-  }
-  const int r = t - first * NT;
-  const int gi = r / (MG * NT);
-  const int gsz = min(MG, m - gi * MG);
-  const int rr = r - gi * MG * NT;
-  nt = rr / gsz;
-  mt = first + gi * MG + rr % gsz;
-}
-
-// Workgroup -> (tile, k-range). Workgroup b runs on XCD b mod 8 as that
-// XCD's (b / 8)-th workgroup. An XCD's whole rounds of kCUsPerXCD tiles run
-// as whole tiles; each tile of its last, partial round is split along K
-// into S parts (S x remainder <= kCUsPerXCD). Parts 0..S-2 leave fp32
-// partial sums in a workspace slot and raise its flag; part S-1 (the
-// highest workgroup index of the tile, so the parts it waits for were
-// dispatched before it) adds them in part order and runs the epilogue.
-struct Job {
-  int e, row0, row_end, nt, S, part, slot0, kt_begin, nk;
-};
-__device__ __forceinline__ bool schedule_tile(const Args& a, int b, Job& j) {
-  const int xcd = b & 7, wi = b >> 3;
-  const int MT = a.tilemap ? a.tilemap[0] : a.max_tiles;
-  const int total = MT * a.n_tiles_n;
-  const int t_lo = (int)((long long)total * xcd / 8);
-  const int t_hi = (int)((long long)total * (xcd + 1) / 8);
-  const int whole = (t_hi - t_lo) / kCUsPerXCD * kCUsPerXCD;
-  const int rem = t_hi - t_lo - whole;
-  const int nk_all = a.K / BK;
-  int tile;
-  j.S = 1;
-  j.part = 0;
-  j.slot0 = 0;
-  if (wi < whole) {
-    tile = t_lo + wi;
-  } else {
-    if (a.split_flags && rem > 0) j.S = min(min(kMaxSplit, kCUsPerXCD / rem), nk_all);
-    const int u = wi - whole;
-    if (u >= rem * j.S) return false;
-    tile = t_lo + whole + u / j.S;
-    j.part = u % j.S;
-    j.slot0 = xcd * kCUsPerXCD + (u / j.S) * (j.S - 1);
-  }
-  int mt;
-  expert_tile_of(tile, MT, a.n_tiles_n, a.tilemap, a.offsets, mt, j.nt);
-  if (a.tilemap) {
-    j.e = a.tilemap[1 + 2 * mt];
-    j.row0 = a.tilemap[2 + 2 * mt];
-    j.row_end = a.offsets[j.e + 1];
-  } else {
-    j.e = 0;
-    j.row0 = mt * TM;
-    j.row_end = a.rows;
-  }
-  j.kt_begin = j.part * nk_all / j.S;
-  j.nk = (j.part + 1) * nk_all / j.S - j.kt_begin;
-  return true;
-}
 
 template <int MODE, bool MX>
 __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
@@ -305,7 +167,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   const int wn = wave & 3;    // column quarter
 
   Job jb;
-  if (!schedule_tile(a, blockIdx.x, jb)) return;
+  if (!schedule_tile<BK>(a, blockIdx.x, jb)) return;
   const int e = jb.e, row0 = jb.row0, row_end = jb.row_end, nt = jb.nt;
   const int S = jb.S, part = jb.part, slot0 = jb.slot0, kt_begin = jb.kt_begin, nk = jb.nk;
   const int K = a.K, N = a.N;
@@ -334,7 +196,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     const int p = 512 * r + tid, m = p >> 2, q = (p & 3) ^ swz4(m);
     int arow = min(row0 + m, row_end - 1);
     if (a.gather) arow = min((unsigned)a.gather[arow], (unsigned)(a.gather_rows - 1));
-    a_g[r] = a.A + (size_t)arow * K + kt_begin * BK + 8 * q;
+    a_g[r] = static_cast<const uint16_t*>(a.A) + (size_t)arow * K + kt_begin * BK + 8 * q;
   }
   // ---- B copies.
   //   bf16: LDS k-row (512 bytes = 32 chunks of 8 columns) slot c holds
@@ -683,59 +545,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
 #undef G_RA
 #undef G_MF
 
-  // ---- split tiles: partial sums through the workspace. A slot holds the
-  // 256 x 256 accumulators in register order, 16 bytes per lane per store:
-  // float4 (wave, q, lane) with q = 4 (2i + j) + r/4 holds acc[i][j][r..r+3].
-  if (S > 1) {
-    float4* mine = reinterpret_cast<float4*>(a.split_ws) + wave * 32 * 64 + lane;
-    if (part < S - 1) {
-      float4* dst = mine + (size_t)(slot0 + part) * (TM * TN / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq)
-            dst[((2 * i + j) * 4 + rq) * 64] =
-                make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
-                            acc[i][j][4 * rq + 3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();  // every wave's partial sums are in memory
-      if (tid == 0) {
-        __hip_atomic_store(a.split_flags + slot0 + part, 1, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-      return;
-    }
-    for (int p = 0; p < S - 1; ++p) {
-      if (tid == 0) {
-        // bounded wait: the part was dispatched before this workgroup and
-        // never waits itself, so the flag rises within its run time
-        for (int spin = 0; spin < (1 << 24); ++spin) {
-          if (__hip_atomic_load(a.split_flags + slot0 + p, __ATOMIC_ACQUIRE,
-                                __HIP_MEMORY_SCOPE_AGENT) != 0)
-            break;
-          __builtin_amdgcn_s_sleep(2);
-        }
-        __hip_atomic_store(a.split_flags + slot0 + p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const float4* src = mine + (size_t)(slot0 + p) * (TM * TN / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const float4 v = src[((2 * i + j) * 4 + rq) * 64];
-            acc[i][j][4 * rq] += v.x;
-            acc[i][j][4 * rq + 1] += v.y;
-            acc[i][j][4 * rq + 2] += v.z;
-            acc[i][j][4 * rq + 3] += v.w;
-          }
-    }
-  }
+  // ---- split tiles: partial sums through the workspace
+  if (S > 1 && !split_exchange(a, jb, acc, wave, lane, tid)) return;
 
   // ---- epilogue through LDS, so that global stores are 16 bytes per lane.
   // Accumulator r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of
@@ -771,35 +582,14 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
       if (grow < row_end && f < N) *reinterpret_cast<u32x4_t*>(H + (size_t)grow * N + f) = v;
     }
   } else {
-    // wave tile: 128 rows x 64 fp32 columns, in two halves of 32 columns
-    unsigned char* wl = smem + wave * (128 * 128);
-    float* Y = static_cast<float*>(a.out);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 32 * i + 8 * (r >> 2) + 4 * lq + (r & 3);
-          *reinterpret_cast<float*>(wl + m * 128 + lrow * 4) = acc[i][j][r];
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int idx = it * 64 + lane, m = idx >> 3, ch = idx & 7;
-        const int grow = row0 + 128 * wm + m, n = n0 + bcol[j] + 4 * ch;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 128 + ch * 16);
-        if (grow < row_end && n < N) *reinterpret_cast<u32x4_t*>(Y + (size_t)grow * N + n) = v;
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half overwrites
-    }
+    store_down_tile(a, acc, smem, wave, lane, row0 + 128 * wm, row_end, n0, bcol);
   }
 }
 
 hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   Args a;
-  a.A = static_cast<const uint16_t*>(p.A);
+  a.A = p.A;
   a.gather = p.gather;
   a.gather_rows = p.gather_rows;
   a.tilemap = p.tilemap;

@@ -1,0 +1,247 @@
+// Tile schedule, operand-copy helpers and the split-tile exchange shared by
+// the grouped GEMM kernels (gemm.hip: bf16 activations; gemm_a8.hip: MXFP8
+// activations with MXFP4 weights). Both compute 256 x 256 tiles with 8
+// waves; they differ in the k covered per step and in the operand formats.
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int TM = kBM;                 // 256 rows per tile
+constexpr int TN = 256;                 // B-columns per tile
+constexpr int kCUsPerXCD = 32;          // MI355X: 256 CUs in 8 XCDs
+constexpr int kMaxSplit = 8;            // K-parts of a split tile
+
+enum { MODE_SWIGLU = 0, MODE_DOWN = 1 };
+
+struct Args {
+  const void* A;          // bf16 rows, or MXFP8 codes (MXFP8 A)
+  const uint8_t* SA;      // MXFP8 A: e8m0 scales [A rows][K/32]
+  const int32_t* gather;  // A row of tile row r: gather[r] (< gather_rows), or r when nullptr
+  int gather_rows;
+  const int32_t* tilemap;
+  const int32_t* offsets;
+  int rows, max_tiles, K, N, n_tiles_n;
+  const void* B0;
+  const void* B1;
+  const uint8_t* S0;
+  const uint8_t* S1;
+  float clamp;
+  void* out;
+  float* split_ws;       // partial accumulators of split tiles, or nullptr
+  int32_t* split_flags;  // one ready flag per partial slot, zero between launches
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Slot permutation of the 4 k-groups of a 64-byte A row: rows r..r+15 then
+// put any one k-group in 16 distinct 16-byte bank groups, and so do rows
+// r..r+3 with all 4 k-groups.
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
+}
+// Asynchronous copies global -> LDS: lane l's 16 bytes land at
+// lds_base + 16 l (dma16); lane l's byte lands, zero-extended to a dword,
+// at lds_base + 4 l (dma1).
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma1(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 1, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `groups` steps of this thread's copies are in flight
+template <int PER>
+__device__ __forceinline__ void wait_copy_groups(int groups) {
+  switch (groups) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<2 * PER>(); break;
+    case 3: wait_vmcnt<3 * PER>(); break;
+    case 4: wait_vmcnt<4 * PER>(); break;
+    case 5: wait_vmcnt<5 * PER>(); break;
+    default: wait_vmcnt<6 * PER>(); break;
+  }
+}
+
+// Tile order, by expert: an expert's tiles are contiguous, in groups of up
+// to 8 of its M-tiles; inside a group N-tile major and M-tile minor. The 32
+// workgroups an XCD runs at once then cover about 8 M-tiles x 4 N-tiles of
+// one expert, so each weight slab is fetched once and shared by all those
+// M-tiles, and each activation slab by 4 N-tiles. With a tile map, M-tile
+// t / NT and the tile's own belong to the same expert (an expert's tiles
+// span whole rows of NT), which gives the expert's first M-tile and count
+// without a search.
+__device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int32_t* tilemap,
+                                               const int32_t* offsets, int& mt, int& nt) {
+  constexpr int MG = 8;
+  int first = 0, m = MT;
+  if (tilemap) {
+    const int g = t / NT;
+    const int e = tilemap[1 + 2 * g];
+    const int seg = offsets[e];
+    first = g - (tilemap[2 + 2 * g] - seg) / TM;
+    m = (offsets[e + 1] - seg + TM - 1) / TM;
+  }
+  const int r = t - first * NT;
+  const int gi = r / (MG * NT);
+  const int gsz = min(MG, m - gi * MG);
+  const int rr = r - gi * MG * NT;
+  nt = rr / gsz;
+  mt = first + gi * MG + rr % gsz;
+}
+
+// Workgroup -> (tile, k-range). Workgroup b runs on XCD b mod 8 as that
+// XCD's (b / 8)-th workgroup. An XCD's whole rounds of kCUsPerXCD tiles run
+// as whole tiles; each tile of its last, partial round is split along K
+// into S parts (S x remainder <= kCUsPerXCD). Parts 0..S-2 leave fp32
+// partial sums in a workspace slot and raise its flag; part S-1 (the
+// highest workgroup index of the tile, so the parts it waits for were
+// dispatched before it) adds them in part order and runs the epilogue.
+struct Job {
+  int e, row0, row_end, nt, S, part, slot0, kt_begin, nk;
+};
+template <int BK>
+__device__ __forceinline__ bool schedule_tile(const Args& a, int b, Job& j) {
+  const int xcd = b & 7, wi = b >> 3;
+  const int MT = a.tilemap ? a.tilemap[0] : a.max_tiles;
+  const int total = MT * a.n_tiles_n;
+  const int t_lo = (int)((long long)total * xcd / 8);
+  const int t_hi = (int)((long long)total * (xcd + 1) / 8);
+  const int whole = (t_hi - t_lo) / kCUsPerXCD * kCUsPerXCD;
+  const int rem = t_hi - t_lo - whole;
+  const int nk_all = a.K / BK;
+  int tile;
+  j.S = 1;
+  j.part = 0;
+  j.slot0 = 0;
+  if (wi < whole) {
+    tile = t_lo + wi;
+  } else {
+    if (a.split_flags && rem > 0) j.S = min(min(kMaxSplit, kCUsPerXCD / rem), nk_all);
+    const int u = wi - whole;
+    if (u >= rem * j.S) return false;
+    tile = t_lo + whole + u / j.S;
+    j.part = u % j.S;
+    j.slot0 = xcd * kCUsPerXCD + (u / j.S) * (j.S - 1);
+  }
+  int mt;
+  expert_tile_of(tile, MT, a.n_tiles_n, a.tilemap, a.offsets, mt, j.nt);
+  if (a.tilemap) {
+    j.e = a.tilemap[1 + 2 * mt];
+    j.row0 = a.tilemap[2 + 2 * mt];
+    j.row_end = a.offsets[j.e + 1];
+  } else {
+    j.e = 0;
+    j.row0 = mt * TM;
+    j.row_end = a.rows;
+  }
+  j.kt_begin = j.part * nk_all / j.S;
+  j.nk = (j.part + 1) * nk_all / j.S - j.kt_begin;
+  return true;
+}
+
+// Split tiles: partial sums through the workspace. A slot holds the
+// 256 x 256 accumulators in register order, 16 bytes per lane per store:
+// float4 (wave, q, lane) with q = 4 (2i + j) + r/4 holds acc[i][j][r..r+3].
+// Parts 0..S-2 store theirs, raise their flag and return false; part S-1
+// adds the others' in part order and returns true (it runs the epilogue).
+__device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, f32x16_t (&acc)[4][2],
+                                               int wave, int lane, int tid) {
+  const int S = jb.S, part = jb.part, slot0 = jb.slot0;
+  float4* mine = reinterpret_cast<float4*>(a.split_ws) + wave * 32 * 64 + lane;
+  if (part < S - 1) {
+    float4* dst = mine + (size_t)(slot0 + part) * (TM * TN / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          dst[((2 * i + j) * 4 + rq) * 64] =
+              make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                          acc[i][j][4 * rq + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();  // every wave's partial sums are in memory
+    if (tid == 0) {
+      __hip_atomic_store(a.split_flags + slot0 + part, 1, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return false;
+  }
+  for (int p = 0; p < S - 1; ++p) {
+    if (tid == 0) {
+      // bounded wait: the part was dispatched before this workgroup and
+      // never waits itself, so the flag rises within its run time
+      for (int spin = 0; spin < (1 << 24); ++spin) {
+        if (__hip_atomic_load(a.split_flags + slot0 + p, __ATOMIC_ACQUIRE,
+                              __HIP_MEMORY_SCOPE_AGENT) != 0)
+          break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __hip_atomic_store(a.split_flags + slot0 + p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const float4* src = mine + (size_t)(slot0 + p) * (TM * TN / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 v = src[((2 * i + j) * 4 + rq) * 64];
+          acc[i][j][4 * rq] += v.x;
+          acc[i][j][4 * rq + 1] += v.y;
+          acc[i][j][4 * rq + 2] += v.z;
+          acc[i][j][4 * rq + 3] += v.w;
+        }
+  }
+  return true;
+}
+
+// Down-projection epilogue: the wave's 128 rows x 64 fp32 columns (rows
+// from wrow0, B-columns n0 + bcol[j] + 0..31) go through the wave's 16 KB of
+// LDS at wl, in two halves of 32 columns, so that the global stores are
+// 16 bytes per lane. Accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32 of its 32x32 tile.
+__device__ __forceinline__ void store_down_tile(const Args& a, const f32x16_t (&acc)[4][2],
+                                                unsigned char* smem, int wave, int lane, int wrow0,
+                                                int row_end, int n0, const int (&bcol)[2]) {
+  const int lrow = lane & 31, lq = lane >> 5, N = a.N;
+  unsigned char* wl = smem + wave * (128 * 128);
+  float* Y = static_cast<float*>(a.out);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * i + 8 * (r >> 2) + 4 * lq + (r & 3);
+        *reinterpret_cast<float*>(wl + m * 128 + lrow * 4) = acc[i][j][r];
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane, m = idx >> 3, ch = idx & 7;
+      const int grow = wrow0 + m, n = n0 + bcol[j] + 4 * ch;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 128 + ch * 16);
+      if (grow < row_end && n < N) *reinterpret_cast<u32x4_t*>(Y + (size_t)grow * N + n) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half overwrites
+  }
+}
+
+}  // namespace
+}  // namespace moe

@@ -53,7 +53,8 @@ hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* til
 // bf16 activations: grouped MFMA GEMMs over the tile map. A dense launch
 // (tilemap == nullptr) treats rows [0, rows) as one segment of expert 0.
 struct GemmProblem {
-  const void* A;           // [rows][K] bf16, or [gather_rows][K] when gathered
+  const void* A;           // [rows][K] bf16 (MXFP8: e4m3 codes), or [gather_rows][K] when gathered
+  const uint8_t* SA;       // MXFP8 A only: e8m0 scales [A rows][K/32]
   const int32_t* gather;   // nullptr, or the A row of each routed row (perm_token)
   int gather_rows;
   const int32_t* tilemap;  // nullptr: dense
@@ -62,18 +63,26 @@ struct GemmProblem {
   int max_tiles;           // M-tiles in the grid
   int K, N;
   int E;
-  const void* B0;          // gate (SwiGLU) or down; [E][K][N] bf16 or MXFP4 codes [E][N][K/2]
+  const void* B0;          // gate (SwiGLU) or down; [E][K][N] bf16 or MXFP4 codes [E][K/32][N][16]
   const void* B1;          // up (SwiGLU), else nullptr
-  const uint8_t* S0;       // MXFP4 scales [E][N][K/32]
+  const uint8_t* S0;       // MXFP4 scales [E][K/32][N]
   const uint8_t* S1;
   int mxfp4;
   float clamp;
-  void* out;               // SwiGLU: H bf16 [rows][N]; down: fp32 [rows][N]
+  void* out;               // SwiGLU: H bf16 [rows][N] (MXFP8 A: codes [rows][N] then
+                           // scales [rows][N/32]); down: fp32 [rows][N]
   float* split_ws;         // kSplitSlots partial-sum slots, or nullptr: no split
   int32_t* split_flags;    // kSplitSlots flags, zero before the launch
 };
 hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);
+
+// MXFP4 weights with MXFP8 activations: rows of bf16 -> MXFP8 (codes
+// [rows][K], scales [rows][K/32]), and the grouped GEMM on the scaled MFMA
+// (gemm_a8.hip).
+hipError_t launch_quant_mxfp8(const void* x, long long rows, int K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+hipError_t launch_gemm_a8(const GemmProblem& p, bool swiglu, hipStream_t s);
 
 // fp32 activations and weights: straightforward VALU kernels.
 hipError_t launch_ffn_f32_gate_up(const moe_cfg& c, const float* x_perm, const int32_t* offsets,

@@ -16,12 +16,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, MXFP4_A8 = 0, 1, 2, 3
 GATE_SOFTMAX, GATE_SIGMOID, GATE_SQRT_SOFTPLUS = 0, 1, 2
 WS_DISPATCH, WS_EXPERT_FFN, WS_FORWARD = 0, 1, 2
 
 _GATING = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID, "sqrt_softplus": GATE_SQRT_SOFTPLUS}
-_DT = {"f32": F32, "fp32": F32, "bf16": BF16, "mxfp4": MXFP4}
+_DT = {"f32": F32, "fp32": F32, "bf16": BF16, "mxfp4": MXFP4, "mxfp4_a8": MXFP4_A8}
 
 
 class MoEError(RuntimeError):
@@ -51,8 +51,8 @@ class _Weights(ctypes.Structure):
 _lib = None
 SYMBOLS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down",
-           "moe_shared_expert", "moe_combine", "moe_forward", "moe_status_string",
-           "moe_last_hip_error", "moe_version"]
+           "moe_shared_expert", "moe_combine", "moe_forward", "moe_quantize_mxfp8",
+           "moe_status_string", "moe_last_hip_error", "moe_version"]
 
 
 def lib():
@@ -75,13 +75,14 @@ def lib():
     L.moe_shared_expert.argtypes = [P, vp, W, vp, vp, vp]
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.moe_forward.argtypes = [P, vp, vp, vp, W, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_quantize_mxfp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_last_hip_error.restype = ctypes.c_int
     L.moe_version.restype = ctypes.c_int
     for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
                  "moe_expert_gate_up", "moe_expert_down", "moe_shared_expert", "moe_combine",
-                 "moe_forward"):
+                 "moe_forward", "moe_quantize_mxfp8"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -207,6 +208,18 @@ def expert_down(cfg: Cfg, H, offsets, weights: Weights, y_perm, ws, stream=None,
     _check(lib().moe_expert_down(ctypes.byref(cfg), _p(H), _p(offsets), ctypes.byref(w),
                                  _p(y_perm), _p(ws), ws.numel(), _stream(stream)))
     return y_perm
+
+
+def quantize_mxfp8(x, codes=None, scales=None, stream=None):
+    """bf16 rows [rows, K] -> MXFP8 (e4m3 codes uint8 [rows, K], e8m0
+    scales uint8 [rows, K/32])."""
+    rows, K = x.shape
+    if codes is None:
+        codes = torch.empty((max(rows, 1), K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((max(rows, 1), K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quantize_mxfp8(_p(x), rows, K, _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
 
 
 def shared_expert(cfg: Cfg, x, weights: Weights, H_shared=None, y_shared=None, stream=None):

@@ -26,6 +26,9 @@ SMALL = {
     "fine128": syn.small_variant(syn.CONFIGS["fine128"], T=256, D=256, F=192),
     "fine384_mxfp4": syn.small_variant(syn.CONFIGS["fine384_mxfp4"], T=200, D=256, F=128,
                                        shared_F=96),
+    # the same layer with MXFP8 activation operands in the routed experts
+    "fine384_mxfp4_a8": syn.small_variant(syn.CONFIGS["fine384_mxfp4_a8"], T=200, D=256, F=128,
+                                          shared_F=96),
 }
 
 
@@ -62,7 +65,7 @@ def test_small_fused_equals_stagewise(name):
 
 
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("name", syn.CONFIG_ORDER)
+@pytest.mark.parametrize("name", syn.CONFIG_ORDER + ["fine384_mxfp4_a8"])
 def test_full_size(name):
     """Full workload, in the launch configuration the benchmark times:
     routing and dispatch on every token, y on sampled tokens."""
