@@ -42,7 +42,9 @@
  *   perm_token int32 [T*k]  token of each segment row (rows < A written)
  *   x_perm   [T*k][D] act dtype  H [T*k][F] act dtype  y_perm [T*k][D] fp32
  *   (MOE_MXFP4_A8: H holds MXFP8, e4m3 codes uint8 [T*k][F] followed by
- *   e8m0 scales uint8 [T*k][F/32], in the same [T*k][F] bf16-sized buffer)
+ *   e8m0 scales uint8 [ceil(F/512)][T*k][16] -- the scale of row r, block
+ *   b at ((b/16)*T*k + r)*16 + b%16, so that 8 GEMM steps of a row's
+ *   scales are one 16-byte piece -- in the same [T*k][F] bf16-sized buffer)
  *   y        [T][D]   act dtype
  * Every device pointer must be 16-byte aligned.
  *

@@ -6,8 +6,8 @@ or overwrites an MFMA destination register right after such a block (a
 register move, a spill), nothing guarantees the wait states the hardware
 needs, and the value read can be stale. This module compiles a HIP source
 to gfx950 assembly and reports every compiler instruction, within the first
-few after an MFMA-terminated asm block, that touches a register one of the
-block's trailing MFMAs writes.
+few after an asm block that issues MFMAs, that touches a register one of the
+block's last MFMAs writes.
 
     python -m mixture_experts_layer_25_amd.asmcheck [source.hip]
 """
@@ -22,6 +22,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 WINDOW = 6  # instructions checked after each block
+PAD = 19    # wait states after which a 16-pass MFMA result is readable
 
 
 def _regs(op: str) -> set:
@@ -51,13 +52,22 @@ def find_hazards(asm: str) -> list[str]:
                 if t and not t.startswith(";"):
                     body.append(t)
                 j += 1
+            # destinations of the block's last MFMAs (up to 8, the most a
+            # block issues back to back), unless the block itself waits
+            # PAD wait states after its last MFMA (s_nop N counts N + 1,
+            # another instruction 1, s_waitcnt nothing)
+            mf = [n for n, t in enumerate(body) if t.startswith("v_mfma")]
             dst = set()
-            for t in reversed(body):
-                if t.startswith("s_waitcnt"):
-                    continue
-                if not t.startswith("v_mfma"):
-                    break
-                dst |= _regs(t.split()[1].rstrip(","))
+            if mf:
+                pad = 0
+                for t in body[mf[-1] + 1:]:
+                    if t.startswith("s_nop"):
+                        pad += int(t.split()[1], 0) + 1
+                    elif not t.startswith("s_waitcnt"):
+                        pad += 1
+                if pad < PAD:
+                    for n in mf[-8:]:
+                        dst |= _regs(body[n].split()[1].rstrip(","))
             if dst:
                 k, n = j + 1, 0
                 while n < WINDOW and k < len(lines) and ";;#ASMSTART" not in lines[k]:
@@ -85,14 +95,20 @@ def compile_to_asm(src: str) -> str:
         return open(out).read()
 
 
+SOURCES = ("gemm.hip", "gemm_a8.hip")
+
+
 def main(argv=None) -> int:
     argv = sys.argv[1:] if argv is None else argv
-    src = argv[0] if argv else os.path.join(HERE, "csrc", "gemm.hip")
-    hazards = find_hazards(compile_to_asm(src))
-    for h in hazards:
-        print(h)
-    print(f"{len(hazards)} MFMA result hazards after asm blocks in {os.path.basename(src)}")
-    return 1 if hazards else 0
+    srcs = argv or [os.path.join(HERE, "csrc", f) for f in SOURCES]
+    total = 0
+    for src in srcs:
+        hazards = find_hazards(compile_to_asm(src))
+        for h in hazards:
+            print(h)
+        print(f"{len(hazards)} MFMA result hazards after asm blocks in {os.path.basename(src)}")
+        total += len(hazards)
+    return 1 if total else 0
 
 
 if __name__ == "__main__":

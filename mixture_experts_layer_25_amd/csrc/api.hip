@@ -56,7 +56,7 @@ int check_weights(const moe_cfg& c, const moe_weights* w) {
   if (!w) return MOE_ERR_INVALID_ARG;
   if (!dev_ok(w->W_gate) || !dev_ok(w->W_up) || !dev_ok(w->W_down)) return MOE_ERR_INVALID_ARG;
   if (is_mx(c)) {
-    if (!w->S_gate || !w->S_up || !w->S_down) return MOE_ERR_INVALID_ARG;
+    if (!dev_ok(w->S_gate) || !dev_ok(w->S_up) || !dev_ok(w->S_down)) return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
 }
@@ -94,9 +94,10 @@ size_t dispatch_ws(const moe_cfg& c) {
 // partial-sum slots of the grouped GEMMs
 size_t tilemap_bytes(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
 size_t ffn_ws(const moe_cfg& c) { return tilemap_bytes(c) + moe::split_bytes(c); }
-// MXFP8 copy of `rows` activation rows of width K: codes, then scales
+// MXFP8 copy of `rows` activation rows of width K: codes, then the scales
+// in the grouped layout the GEMM reads ([ceil(K/512)][rows][16])
 size_t mxfp8_bytes(size_t rows, int K) {
-  return moe::align_up(rows * K, kAlign) + moe::align_up(rows * (K / 32), kAlign);
+  return moe::align_up(rows * K, kAlign) + moe::align_up((size_t)((K + 511) / 512) * rows * 16, kAlign);
 }
 // the stage entry points' FFN workspace: with MXFP8 activations, the
 // quantised x_perm follows the tile map and split slots
@@ -189,7 +190,7 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gath
   if (!is_a8(c)) return moe::launch_gemm_swiglu(g, s);
   const long long qrows = gather ? c.T : (long long)c.T * c.top_k;
   uint8_t* xs = xq + moe::align_up((size_t)qrows * c.D, kAlign);
-  e = moe::launch_quant_mxfp8(x_perm, qrows, c.D, xq, xs, s);
+  e = moe::launch_quant_mxfp8(x_perm, qrows, c.D, xq, xs, true, s);
   if (e != hipSuccess) return e;
   g.A = xq;
   g.SA = xs;
@@ -215,7 +216,7 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
   g.S0 = w.S_down;
   g.out = y_perm;
   if (!is_a8(c)) return moe::launch_gemm_down(g, s);
-  g.SA = static_cast<const uint8_t*>(H) + (size_t)g.rows * c.F;  // MXFP8 H: scales after codes
+  g.SA = static_cast<const uint8_t*>(H) + (size_t)g.rows * c.F;  // MXFP8 H: grouped scales after codes
   return moe::launch_gemm_a8(g, false, s);
 }
 
@@ -381,7 +382,7 @@ int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, u
   if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
   if (!dev_ok(x) || !dev_ok(codes) || !dev_ok(scales)) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
-  return hip_status(moe::launch_quant_mxfp8(x, rows, K, codes, scales,
+  return hip_status(moe::launch_quant_mxfp8(x, rows, K, codes, scales, false,
                                             static_cast<hipStream_t>(stream)));
 }
 

@@ -67,10 +67,6 @@
 // workspace in a fixed order.
 #include "gemm_tile.h"
 
-// The asm blocks that issue LDS copies set M0 themselves and list it as
-// clobbered; clang warns about clobbering a reserved register.
-#pragma clang diagnostic ignored "-Winline-asm"
-
 namespace moe {
 namespace {
 
@@ -148,10 +144,6 @@ __device__ __forceinline__ void mx_fragments(uint32_t c0, uint32_t s0, uint32_t 
 }
 
 
-// Wait states after an asm block's last MFMA so that whatever the compiler
-// places next (a register move, a spill, a VALU read) sees the finished
-// accumulator: the compiler does not look inside asm for MFMA hazards.
-#define MFMA_TAIL "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
 
 
 template <int MODE, bool MX>

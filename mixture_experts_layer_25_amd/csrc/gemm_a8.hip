@@ -15,7 +15,9 @@
 // the block's exponent is floor(log2(max |v|)) - 8 (8: the exponent of
 // e4m3's largest normal), clamped to the e8m0 range; each element is v
 // times 2^-exponent, saturated to +-448 and rounded to nearest even by
-// v_cvt_pk_fp8_f32.
+// v_cvt_pk_fp8_f32. Scales are stored row-major ([rows][K/32]) or, for the
+// GEMM, grouped: [ceil(K/512)][rows][16] (the 16 scales of 8 GEMM steps of
+// a row in one 16-byte piece).
 //
 // gemm_a8_kernel<MODE>: the tile schedule and tile shape of the bf16 kernel
 // (256 x 256 tiles, 8 waves, wave (wm, wn) owns rows 128wm.. and B-columns
@@ -24,17 +26,22 @@
 // lane l supplies row l%32 of A with k = 16h..16h+15 and 32+16h..32+16h+15
 // (h = l/32) in its 8 registers, column l%32 of B with k = 32h..32h+31 in
 // its 4 registers, and the e8m0 scales of row (column) l%32, k-block h.
-// Per step and stage (28 KB, 5 stages):
+// Per step and stage (24.5 KB, 5 stages):
 //   A codes  256 rows x 64 bytes, 16-byte k-groups swizzled as in the bf16
 //            kernel (slot = group ^ swz4(row)); a lane reads groups h, h+2;
-//   A scales 2 blocks x 256 rows, a dword each;
 //   B codes  2 blocks x 256 columns x 16 bytes (block-major storage: one
 //            contiguous run per block and weight matrix);
-//   B scales 2 blocks x 256 columns, a dword each.
-// Every operand byte goes global -> LDS with global_load_lds (5 copies per
-// thread and step). One barrier per step; each step's LDS reads sit in one
-// asm block that waits for them (the compiler cannot tell the fragment
-// reads from the copies in flight), then the step's 8 MFMAs.
+//   B scales 2 blocks x 256 columns, one byte each (copied as dwords).
+// A scales: a ring of 3 groups of 8 steps (16 bytes per row, 4 KB each).
+// Every operand byte goes global -> LDS with global_load_lds. A copy
+// instruction costs about the same whatever its width (measured: one byte
+// per lane from 64 rows cost as much per instruction as 16 bytes), so the
+// scales travel in as few instructions as possible: per step and CU 16
+// instructions of A, 8 of B codes, 2 of B scales and half of one of A
+// scales, against 40 when every scale byte had a lane of its own. One
+// barrier per step. A step is two halves of 4 MFMAs (row tiles 0-1, then
+// 2-3); each half is one asm block whose LDS reads (the other half's
+// fragments) sit between its MFMAs.
 // Epilogues: SwiGLU forms h = SiLU(clamp(g)) * clamp(u) in fp32 and writes
 // it as MXFP8 (each wave's 32 f-columns of a row are one block: codes
 // [rows][F] and scales [rows][F/32]); down stores fp32 rows.
@@ -44,18 +51,59 @@ namespace moe {
 namespace {
 
 constexpr int BK8 = 64;                    // k per step
-constexpr int A8_BYTES = TM * BK8;         // 16 KB of A codes
-constexpr int A8S_BYTES = 2 * TM * 4;      // 2 KB of A scales
-constexpr int B8C_BYTES = 2 * TN * 16;     // 8 KB of B codes
-constexpr int B8S_BYTES = 2 * TN * 4;      // 2 KB of B scales
-constexpr int SB8 = A8_BYTES + A8S_BYTES + B8C_BYTES + B8S_BYTES;
-constexpr int NST8 = 5;                    // 140 KB of the 160 KB LDS
-constexpr int PER8 = 5;                    // copies per thread per step
-static_assert(NST8 * SB8 <= 160 * 1024, "LDS");
-static_assert(NST8 * SB8 >= 8 * 128 * 128, "the epilogue stages 16 KB per wave");
+constexpr int A8_BYTES = TM * BK8;         // 16 KB of A codes per step
+constexpr int B8C_BYTES = 2 * TN * 16;     // 8 KB of B codes per step
+constexpr int B8S_BYTES = 2 * TN;          // 512 B of B scales per step
+constexpr int SB8 = A8_BYTES + B8C_BYTES + B8S_BYTES;
+constexpr int NST8 = 5;                    // operand stages
+constexpr int kSG = 8;                     // steps per A-scale group
+constexpr int ASG_BYTES = TM * 16;         // one group of A scales: 16 bytes per row
+constexpr int AS_OFF = NST8 * SB8;         // ring of 3 A-scale groups after the stages
+constexpr int LDS8 = AS_OFF + 3 * ASG_BYTES;  // 134.5 KB of the 160 KB LDS
+static_assert(LDS8 <= 160 * 1024, "LDS");
+static_assert(LDS8 >= 8 * 128 * 128, "the epilogue stages 16 KB per wave");
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte offset of the e8m0 scale of (row, 32-element block kb) in the
+// grouped scale layout the GEMM reads: [ceil(K/512)][rows][16], i.e. for
+// each run of 16 blocks (8 GEMM steps) every row's 16 scales are one
+// 16-byte piece, copied by one lane.
+__device__ __forceinline__ size_t grouped_scale(long long row, int kb, long long rows) {
+  return ((size_t)(kb / 16) * rows + row) * 16 + kb % 16;
+}
+
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) for a count known only at run time (n <= 15)
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;
+  }
+}
+
+// the two 16-byte halves of an MFMA A operand as one 8-register value
+__device__ __forceinline__ i32x8_t join8(i32x4_t lo, i32x4_t hi) {
+  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 
 // Two floats -> two e4m3 codes in the low (HI = false) or high 16 bits of
 // `old`, saturated to +-448, rounded to nearest even.
@@ -88,12 +136,13 @@ __device__ __forceinline__ uint32_t mxfp8_block(const float (&v)[32], uint32_t (
   return (uint32_t)s;
 }
 
+template <bool GROUPED>
 __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x,
-                                                          long long nblocks,
+                                                          long long rows, int KB,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
   const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
+  if (b >= rows * KB) return;
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + b * 32);
   float v[32];
 #pragma unroll
@@ -110,12 +159,12 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __rest
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + b * 32);
   dst[0] = u32x4_t{q[0], q[1], q[2], q[3]};
   dst[1] = u32x4_t{q[4], q[5], q[6], q[7]};
-  scales[b] = (uint8_t)s;
+  scales[GROUPED ? grouped_scale(b / KB, (int)(b % KB), rows) : (size_t)b] = (uint8_t)s;
 }
 
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NST8 * SB8];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS8];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -147,7 +196,13 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
     return r;
   };
 
-  // ---- copy sources (advanced by one step per issue) and LDS offsets
+  // ---- copy sources and destinations. Per step and thread: two 16-byte
+  // pieces of A and one of B codes; waves 0 and 1 also copy the step's two
+  // blocks of B scales (one dword per lane: 4 columns). The A scales come
+  // in groups of 8 steps (16 bytes per row, grouped layout): wave w < 4
+  // copies its 64 rows of group G + 2 at the step of group G whose index
+  // within the group is w, into a ring of 3 group buffers; the first
+  // groups of the tile's k-range are copied before the loop.
   const uint8_t* A = static_cast<const uint8_t*>(a.A);
   const uint8_t* a_g[2];
 #pragma unroll
@@ -156,26 +211,41 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
     a_g[r] = A + (size_t)a_row(m) * K + kt_begin * BK8 + 16 * q;
   }
   const int blk = tid >> 8, c = tid & 255;
-  const uint8_t* as_g = a.SA + (size_t)a_row(c) * KB + 2 * kt_begin + blk;
   const uint8_t* bc_g;
-  const uint8_t* bs_g;
   {
     bool up;
     const int col = b_column(c, up);
     const size_t bi = ((size_t)e * KB + 2 * kt_begin + blk) * N + col;
     bc_g = static_cast<const uint8_t*>(up ? a.B1 : a.B0) + bi * 16;
-    bs_g = (up ? a.S1 : a.S0) + bi;
   }
-  const size_t bc_step = (size_t)2 * N * 16, bs_step = (size_t)2 * N;
+  const size_t bc_step = (size_t)2 * N * 16;
+  // B scales: wave b < 2 copies block b of each step, lane l the 4 columns
+  // of tile columns 4l.. (SwiGLU: gate for l < 32, up for l >= 32)
+  const uint8_t* bs_g = nullptr;
+  if (wave < 2) {
+    const bool up = MODE == MODE_SWIGLU && lane >= 32;
+    int col = MODE == MODE_SWIGLU ? n0 + 4 * (lane & 31) : n0 + 4 * lane;
+    if (col >= N) col = 0;  // any valid columns; never stored
+    bs_g = (up ? a.S1 : a.S0) + ((size_t)e * KB + 2 * kt_begin + wave) * N + col;
+  }
+  const size_t bs_step = (size_t)2 * N;
+  // A scales: row 64 w + lane of the tile, grouped layout
+  const long long sa_rows = a.gather ? a.gather_rows : a.rows;
+  const uint8_t* as_g = wave < 4 ? a.SA + (size_t)a_row(64 * wave + lane) * 16 : nullptr;
+  const int g_last = (kt_begin + nk - 1) / kSG;  // last group of the k-range
+  auto issue_group = [&](int g) __attribute__((always_inline)) {
+    g = min(g, g_last);  // past the range: copy the last group again (same bytes)
+    dma16(as_g + (size_t)g * sa_rows * 16, smem + AS_OFF + (g % 3) * ASG_BYTES + wave * 1024);
+  };
   auto issue = [&](int kt, uint32_t so) __attribute__((always_inline)) {
     unsigned char* st = smem + so;
     const int k = kt - kt_begin;
     dma16(a_g[0] + k * BK8, st + wave * 1024);
     dma16(a_g[1] + k * BK8, st + 8192 + wave * 1024);
-    dma1(as_g + 2 * k, st + A8_BYTES + wave * 256);
-    dma16(bc_g + k * bc_step, st + A8_BYTES + A8S_BYTES + wave * 1024);
-    dma1(bs_g + k * bs_step, st + A8_BYTES + A8S_BYTES + B8C_BYTES + wave * 256);
+    dma16(bc_g + k * bc_step, st + A8_BYTES + wave * 1024);
+    if (wave < 2) dma4(bs_g + k * bs_step, st + A8_BYTES + B8C_BYTES + wave * 256);
   };
+  const int per = wave < 2 ? 4 : 3;  // this wave's copies per step
 
   int bcol[2];
   if (MODE == MODE_SWIGLU) {
@@ -195,89 +265,189 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int lrow = lane & 31, h = lane >> 5;
-  // per-lane LDS addresses in stage 0 (fragment i of A is 32 rows = 2048
-  // bytes, and its scales 128 bytes, further; swz4 repeats every 32 rows)
+  // per-lane LDS addresses: operands in stage 0 (fragment i of A is 32
+  // rows = 2048 bytes further; swz4 repeats every 32 rows), A scales in
+  // group buffer 0 at step 0 of the group (fragment i: 512 bytes further)
   const uint32_t base = lds_addr(smem);
   uint32_t a_lo, a_hi, as_a, bc_a[2], bs_a[2];
   {
     const int m = 128 * wm + lrow;
     a_lo = base + m * 64 + ((h ^ swz4(m)) * 16);
     a_hi = base + m * 64 + (((h + 2) ^ swz4(m)) * 16);
-    as_a = base + A8_BYTES + h * 1024 + m * 4;
+    as_a = base + AS_OFF + m * 16 + h;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = bcol[j] + lrow;
-      bc_a[j] = base + A8_BYTES + A8S_BYTES + h * 4096 + col * 16;
-      bs_a[j] = base + A8_BYTES + A8S_BYTES + B8C_BYTES + h * 1024 + col * 4;
+      bc_a[j] = base + A8_BYTES + h * 4096 + col * 16;
+      bs_a[j] = base + A8_BYTES + B8C_BYTES + h * 256 + col;
     }
   }
+  // A-scale offset of absolute step t: group buffer (t / 8) % 3, 2 bytes a step
+  auto as_off = [](int t) { return (uint32_t)((t / kSG) % 3 * ASG_BYTES + (t % kSG) * 2); };
 
   // a wave whose rows all lie past the segment end keeps copying and
   // synchronising but skips its reads and MFMAs
   const bool idle = __builtin_amdgcn_readfirstlane(row_end - row0 <= 128 * wm) != 0;
 
-#pragma unroll
-  for (int s = 0; s < NST8 - 1; ++s)
-    if (s < nk) issue(kt_begin + s, s * SB8);
+  // Fragments. A step is two halves: rows 0-63 of the wave (MFMA row tiles
+  // 0, 1; set P) and rows 64-127 (tiles 2, 3; set Q). The MFMAs of one half
+  // run in one asm block with LDS reads between them; the block ends by
+  // waiting for its reads, so no load stays in flight outside the block that
+  // issued it. The first half reads Q of the same step; the second half
+  // reads P of the next step between its MFMAs and, after its last MFMA,
+  // the next step's B fragments (16 code bytes of block h per column tile)
+  // and B scales into the registers its MFMAs have just read. A rows
+  // 32i + lrow: k-groups h (l) and h + 2 (g), joined into one 8-register
+  // operand; scales one dword each. Read addresses are formed inside the
+  // blocks (lane base + stage offset) in two alternating registers.
+  i32x4_t pl0, pg0, pl1, pg1, ql0, qg0, ql1, qg1, b0, b1;
+  int sa0, sa1, sa2, sa3, t0, t1;
+#define A8_MF(I, J, AR, BR, SA, SB)                                                  \
+  "v_mfma_scale_f32_32x32x64_f8f6f4 %[c" #I #J "], %[" AR "], %[" BR "], %[c" #I #J   \
+  "], %[" SA "], %[" SB "] op_sel_hi:[0,0,0] blgp:4\n\t"
+  // MFMAs of tiles I0, I1 (A operands a0, a1; scales s0, s1) on B b0, b1
+  // (scales t0, t1), with the reads R0..R3 between them and R4 after them
+#define A8_HALF(I0, I1, R0, R1, R2, R3, R4)                                          \
+  A8_MF(I0, 0, "a0", "b0", "s0", "t0") R0 A8_MF(I0, 1, "a0", "b1", "s0", "t1") R1      \
+  A8_MF(I1, 0, "a1", "b0", "s1", "t0") R2 A8_MF(I1, 1, "a1", "b1", "s1", "t1") R3 R4
+#define A8_HALF_X(...) A8_HALF(__VA_ARGS__)  // expands a read list into R0..R4
+  // read OUT (16 or 4 bytes) at lane base ADDR + stage offset (register so)
+  // + OFF, forming the address in register TMP
+#define A8_R(OUT, ADDR, OFF, TMP)                                                    \
+  "v_add_u32 %[" TMP "], %[so], %[" ADDR "]\n\t"                                     \
+  "ds_read_b128 %[" OUT "], %[" TMP "] offset:" OFF "\n\t"
+  // read one scale byte at lane base ADDR + offset register OREG + OFF
+#define A8_RB(OUT, ADDR, OREG, OFF, TMP)                                             \
+  "v_add_u32 %[" TMP "], %[" OREG "], %[" ADDR "]\n\t"                               \
+  "ds_read_u8 %[" OUT "], %[" TMP "] offset:" OFF "\n\t"
+  // Q of this step (A rows 64.., their scales 1024..)
+#define A8_RQ                                                                        \
+  A8_R("nl0", "alo", "4096", "u0") A8_R("ng0", "ahi", "4096", "u1"),                 \
+      A8_R("nl1", "alo", "6144", "u0") A8_R("ng1", "ahi", "6144", "u1"),             \
+      A8_RB("ns0", "as", "ao", "1024", "u0"), A8_RB("ns1", "as", "ao", "1536", "u1"), ""
+  // P of the next step, then (after the last MFMA) its B fragments and scales
+#define A8_RP                                                                        \
+  A8_R("nl0", "alo", "0", "u0") A8_R("ng0", "ahi", "0", "u1"),                       \
+      A8_R("nl1", "alo", "2048", "u0") A8_R("ng1", "ahi", "2048", "u1"),             \
+      A8_RB("ns0", "as", "ao", "0", "u0"), A8_RB("ns1", "as", "ao", "512", "u1"),    \
+      A8_R("b0", "bc0", "0", "u0") A8_R("b1", "bc1", "0", "u1")                      \
+      A8_RB("t0", "bs0", "so", "0", "u0") A8_RB("t1", "bs1", "so", "0", "u1")
+#define A8_BASES                                                                     \
+  [alo] "v"(a_lo), [ahi] "v"(a_hi), [bc0] "v"(bc_a[0]), [bc1] "v"(bc_a[1]),          \
+      [as] "v"(as_a), [bs0] "v"(bs_a[0]), [bs1] "v"(bs_a[1])
+#define A8_ACC                                                                       \
+  [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]),               \
+      [c11] "+v"(acc[1][1]), [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]),           \
+      [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1])
+  uint32_t u0, u1;  // address registers of the blocks
+  // first half of step kt (stage offset SO, A-scale offset AO): tiles 0, 1
+  // from P; reads Q
+#define A8_H1(SO, AO)                                                                \
+  asm volatile("s_nop 4\n\t" A8_HALF_X(0, 1, A8_RQ) "s_waitcnt lgkmcnt(0)"           \
+               : [nl0] "=&v"(ql0), [ng0] "=&v"(qg0), [nl1] "=&v"(ql1), [ng1] "=&v"(qg1), \
+                 [ns0] "=&v"(sa2), [ns1] "=&v"(sa3), [u0] "=&v"(u0), [u1] "=&v"(u1),  \
+                 A8_ACC                                                              \
+               : [a0] "v"(join8(pl0, pg0)), [a1] "v"(join8(pl1, pg1)), [b0] "v"(b0),  \
+                 [b1] "v"(b1), [s0] "v"(sa0), [s1] "v"(sa1), [t0] "v"(t0), [t1] "v"(t1), \
+                 [so] "s"(SO), [ao] "s"(AO), A8_BASES                                \
+               : "memory")
+  // second half: tiles 2, 3 from Q; reads P, B and B scales of the next
+  // step (stage offset SO, A-scale offset AO)
+#define A8_H2(SO, AO)                                                                \
+  asm volatile("s_nop 4\n\t" A8_HALF_X(2, 3, A8_RP) "s_waitcnt lgkmcnt(0)"           \
+               : [nl0] "=&v"(pl0), [ng0] "=&v"(pg0), [nl1] "=&v"(pl1), [ng1] "=&v"(pg1), \
+                 [ns0] "=&v"(sa0), [ns1] "=&v"(sa1), [u0] "=&v"(u0), [u1] "=&v"(u1),  \
+                 [b0] "+v"(b0), [b1] "+v"(b1), [t0] "+v"(t0), [t1] "+v"(t1), A8_ACC   \
+               : [a0] "v"(join8(ql0, qg0)), [a1] "v"(join8(ql1, qg1)), [s0] "v"(sa2), \
+                 [s1] "v"(sa3), [so] "s"(SO), [ao] "s"(AO), A8_BASES                 \
+               : "memory")
+#define A8_H2_LAST()                                                                 \
+  asm volatile("s_nop 4\n\t" A8_HALF(2, 3, "", "", "", "", "") MFMA_TAIL             \
+               : A8_ACC                                                              \
+               : [a0] "v"(join8(ql0, qg0)), [a1] "v"(join8(ql1, qg1)), [b0] "v"(b0),  \
+                 [b1] "v"(b1), [s0] "v"(sa2), [s1] "v"(sa3), [t0] "v"(t0), [t1] "v"(t1))
+  // Step kt of a wave with rows in the segment: first half; then wait until
+  // steps <= kt + 1 have landed and barrier (every wave is then done reading
+  // the stage of step kt, which takes step kt + NST8); then the second
+  // half. Waves past the segment end run the same waits, barriers and
+  // copies.
+  // The wait: this wave's copies issued after those of step kt + 1 may stay
+  // in flight (they complete in order): the step batches of kt + 2 ..
+  // kt + NST8 - 1 and the A-scale group copies of the syncs of steps
+  // kt - NST8 + 1 .. kt - 1 (each sync issues its batch, then its group copy).
+#define A8_SYNC()                                                                    \
+  do {                                                                               \
+    int n = per * (min(nk - 1, kt + NST8 - 1) - min(kt + 1, nk - 1));                \
+    const int lo = max(0, kt - (NST8 - 1)), hi = kt - 1;                             \
+    if (wave < 4 && hi >= lo)                                                        \
+      n += ((wave - (kt_begin + lo) % kSG + kSG) % kSG) <= hi - lo;                  \
+    wait_vmcnt_dyn(n);                                                               \
+    __builtin_amdgcn_s_barrier();                                                    \
+    asm volatile("" ::: "memory");                                                   \
+    if (kt + NST8 < nk) issue(kt_begin + kt + NST8, so);                             \
+    if (wave < 4 && (kt_begin + kt) % kSG == wave) issue_group((kt_begin + kt) / kSG + 2); \
+  } while (0)
 
-  uint32_t so = 0;                           // stage of step kt
-  uint32_t si = (uint32_t)(NST8 - 1) * SB8;  // stage of step kt + NST8 - 1
-  for (int kt = 0; kt < nk; ++kt) {
-    // copies of step kt have landed (steps up to kt + NST8 - 2 were issued)
-    wait_copy_groups<PER8>(min(nk - 1, kt + NST8 - 2) - kt);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // every wave is done reading step kt - 1, whose stage takes step kt + NST8 - 1
-    if (kt + NST8 - 1 < nk) issue(kt_begin + kt + NST8 - 1, si);
-    if (!idle) {
-      i32x4_t l0, l1, l2, l3, g0, g1, g2, g3, b0, b1;
-      int s0, s1, s2, s3, t0, t1;
-      asm volatile(
-          "s_nop 4\n\t"
-          "ds_read_b128 %[l0], %[alo]\n\t"
-          "ds_read_b128 %[g0], %[ahi]\n\t"
-          "ds_read_b128 %[l1], %[alo] offset:2048\n\t"
-          "ds_read_b128 %[g1], %[ahi] offset:2048\n\t"
-          "ds_read_b128 %[l2], %[alo] offset:4096\n\t"
-          "ds_read_b128 %[g2], %[ahi] offset:4096\n\t"
-          "ds_read_b128 %[l3], %[alo] offset:6144\n\t"
-          "ds_read_b128 %[g3], %[ahi] offset:6144\n\t"
-          "ds_read_b128 %[b0], %[bc0]\n\t"
-          "ds_read_b128 %[b1], %[bc1]\n\t"
-          "ds_read_b32 %[s0], %[as]\n\t"
-          "ds_read_b32 %[s1], %[as] offset:128\n\t"
-          "ds_read_b32 %[s2], %[as] offset:256\n\t"
-          "ds_read_b32 %[s3], %[as] offset:384\n\t"
-          "ds_read_b32 %[t0], %[bs0]\n\t"
-          "ds_read_b32 %[t1], %[bs1]\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : [l0] "=&v"(l0), [l1] "=&v"(l1), [l2] "=&v"(l2), [l3] "=&v"(l3), [g0] "=&v"(g0),
-            [g1] "=&v"(g1), [g2] "=&v"(g2), [g3] "=&v"(g3), [b0] "=&v"(b0), [b1] "=&v"(b1),
-            [s0] "=&v"(s0), [s1] "=&v"(s1), [s2] "=&v"(s2), [s3] "=&v"(s3), [t0] "=&v"(t0),
-            [t1] "=&v"(t1)
-          : [alo] "v"(a_lo + so), [ahi] "v"(a_hi + so), [bc0] "v"(bc_a[0] + so),
-            [bc1] "v"(bc_a[1] + so), [as] "v"(as_a + so), [bs0] "v"(bs_a[0] + so),
-            [bs1] "v"(bs_a[1] + so)
-          : "memory");
-      const i32x8_t fa[4] = {
-          i32x8_t{l0[0], l0[1], l0[2], l0[3], g0[0], g0[1], g0[2], g0[3]},
-          i32x8_t{l1[0], l1[1], l1[2], l1[3], g1[0], g1[1], g1[2], g1[3]},
-          i32x8_t{l2[0], l2[1], l2[2], l2[3], g2[0], g2[1], g2[2], g2[3]},
-          i32x8_t{l3[0], l3[1], l3[2], l3[3], g3[0], g3[1], g3[2], g3[3]}};
-      const i32x8_t fb[2] = {i32x8_t{b0[0], b0[1], b0[2], b0[3], 0, 0, 0, 0},
-                             i32x8_t{b1[0], b1[1], b1[2], b1[3], 0, 0, 0, 0}};
-      const int sa[4] = {s0, s1, s2, s3};
-      const int sb[2] = {t0, t1};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], 0 /* A e4m3 */, 4 /* B e2m1 */, 0, sa[i], 0, sb[j]);
-    }
-    so = so + SB8 == NST8 * SB8 ? 0u : so + SB8;
-    si = si + SB8 == NST8 * SB8 ? 0u : si + SB8;
+  // the first A-scale groups, then the copies of the first NST8 steps
+  if (wave < 4) {
+    const int g0 = kt_begin / kSG;
+    issue_group(g0);
+    issue_group(g0 + 1);
+    issue_group(g0 + 2);
   }
+#pragma unroll
+  for (int s = 0; s < NST8; ++s)
+    if (s < nk) issue(kt_begin + s, s * SB8);
+  wait_vmcnt_dyn(per * min(nk - 1, NST8 - 1));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int kt = 0;
+  uint32_t so = 0;  // stage offset of step kt
+  auto next_stage = [](uint32_t o) { return o + SB8 == NST8 * SB8 ? 0u : o + SB8; };
+  if (idle) {
+    for (; kt < nk; ++kt) {
+      A8_SYNC();
+      so = next_stage(so);
+    }
+  } else {
+    // step 0's P, B and scales
+    asm volatile(A8_R("nl0", "alo", "0", "u0") A8_R("ng0", "ahi", "0", "u1")
+                 A8_R("nl1", "alo", "2048", "u0") A8_R("ng1", "ahi", "2048", "u1")
+                 A8_R("nb0", "bc0", "0", "u0") A8_R("nb1", "bc1", "0", "u1")
+                 A8_RB("ns0", "as", "ao", "0", "u0") A8_RB("ns1", "as", "ao", "512", "u1")
+                 A8_RB("nt0", "bs0", "so", "0", "u0") A8_RB("nt1", "bs1", "so", "0", "u1")
+                 "s_waitcnt lgkmcnt(0)"
+                 : [nl0] "=&v"(pl0), [ng0] "=&v"(pg0), [nl1] "=&v"(pl1), [ng1] "=&v"(pg1),
+                   [nb0] "=&v"(b0), [nb1] "=&v"(b1), [ns0] "=&v"(sa0), [ns1] "=&v"(sa1),
+                   [nt0] "=&v"(t0), [nt1] "=&v"(t1), [u0] "=&v"(u0), [u1] "=&v"(u1)
+                 : [so] "s"(0u), [ao] "s"(as_off(kt_begin)), A8_BASES
+                 : "memory");
+    for (; kt + 1 < nk; ++kt) {
+      const uint32_t so1 = next_stage(so);
+      A8_H1(so, as_off(kt_begin + kt));
+      A8_SYNC();
+      A8_H2(so1, as_off(kt_begin + kt + 1));
+      so = so1;
+    }
+    A8_H1(so, as_off(kt_begin + kt));
+    A8_SYNC();
+    A8_H2_LAST();
+  }
+  // the last MFMAs finish writing the accumulators before any VALU reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#undef A8_SYNC
+#undef A8_H2_LAST
+#undef A8_H2
+#undef A8_H1
+#undef A8_ACC
+#undef A8_BASES
+#undef A8_RP
+#undef A8_RQ
+#undef A8_RB
+#undef A8_R
+#undef A8_HALF_X
+#undef A8_HALF
+#undef A8_MF
 
   if (jb.S > 1 && !split_exchange(a, jb, acc, wave, lane, tid)) return;
 
@@ -302,7 +472,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own wave's tile only
     uint8_t* Hc = static_cast<uint8_t*>(a.out);
-    uint8_t* Hs = Hc + (size_t)a.rows * N;  // scales follow the codes
+    uint8_t* Hs = Hc + (size_t)a.rows * N;  // grouped scales follow the codes
     const int f0 = n0 + 32 * wn;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -323,7 +493,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(Hc + (size_t)grow * N + f0);
         dst[0] = u32x4_t{q[0], q[1], q[2], q[3]};
         dst[1] = u32x4_t{q[4], q[5], q[6], q[7]};
-        Hs[(size_t)grow * (N / 32) + f0 / 32] = (uint8_t)s;
+        Hs[grouped_scale(grow, f0 / 32, a.rows)] = (uint8_t)s;
       }
     }
   } else {
@@ -334,11 +504,13 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
 }  // namespace
 
 hipError_t launch_quant_mxfp8(const void* x, long long rows, int K, uint8_t* codes, uint8_t* scales,
-                              hipStream_t s) {
+                              bool grouped, hipStream_t s) {
   const long long nb = rows * (K / 32);
   if (nb <= 0) return hipSuccess;
-  quant_mxfp8_kernel<<<(unsigned)ceil_div(nb, 256), 256, 0, s>>>(static_cast<const uint16_t*>(x),
-                                                                 nb, codes, scales);
+  const unsigned grid = (unsigned)ceil_div(nb, 256);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (grouped) quant_mxfp8_kernel<true><<<grid, 256, 0, s>>>(xb, rows, K / 32, codes, scales);
+  else quant_mxfp8_kernel<false><<<grid, 256, 0, s>>>(xb, rows, K / 32, codes, scales);
   return hipGetLastError();
 }
 

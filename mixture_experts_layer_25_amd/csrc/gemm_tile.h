@@ -7,6 +7,15 @@
 #include "common.h"
 #include "launch.h"
 
+// The bf16 kernel's asm blocks that issue LDS copies set M0 themselves and
+// list it as clobbered; clang warns about clobbering a reserved register.
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// Wait states after an asm block's last MFMA so that whatever the compiler
+// places next (a register move, a spill, a VALU read) sees the finished
+// accumulator: the compiler does not look inside asm for MFMA hazards.
+#define MFMA_TAIL "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+
 namespace moe {
 namespace {
 
@@ -19,7 +28,7 @@ enum { MODE_SWIGLU = 0, MODE_DOWN = 1 };
 
 struct Args {
   const void* A;          // bf16 rows, or MXFP8 codes (MXFP8 A)
-  const uint8_t* SA;      // MXFP8 A: e8m0 scales [A rows][K/32]
+  const uint8_t* SA;      // MXFP8 A: e8m0 scales, grouped [ceil(K/512)][A rows][16]
   const int32_t* gather;  // A row of tile row r: gather[r] (< gather_rows), or r when nullptr
   int gather_rows;
   const int32_t* tilemap;

@@ -54,7 +54,7 @@ hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* til
 // (tilemap == nullptr) treats rows [0, rows) as one segment of expert 0.
 struct GemmProblem {
   const void* A;           // [rows][K] bf16 (MXFP8: e4m3 codes), or [gather_rows][K] when gathered
-  const uint8_t* SA;       // MXFP8 A only: e8m0 scales [A rows][K/32]
+  const uint8_t* SA;       // MXFP8 A only: e8m0 scales, grouped [ceil(K/512)][A rows][16]
   const int32_t* gather;   // nullptr, or the A row of each routed row (perm_token)
   int gather_rows;
   const int32_t* tilemap;  // nullptr: dense
@@ -70,7 +70,7 @@ struct GemmProblem {
   int mxfp4;
   float clamp;
   void* out;               // SwiGLU: H bf16 [rows][N] (MXFP8 A: codes [rows][N] then
-                           // scales [rows][N/32]); down: fp32 [rows][N]
+                           // grouped scales [ceil(N/512)][rows][16]); down: fp32 [rows][N]
   float* split_ws;         // kSplitSlots partial-sum slots, or nullptr: no split
   int32_t* split_flags;    // kSplitSlots flags, zero before the launch
 };
@@ -80,8 +80,9 @@ hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);
 // MXFP4 weights with MXFP8 activations: rows of bf16 -> MXFP8 (codes
 // [rows][K], scales [rows][K/32]), and the grouped GEMM on the scaled MFMA
 // (gemm_a8.hip).
+// (grouped: scales [ceil(K/512)][rows][16], the layout the GEMM reads; else [rows][K/32])
 hipError_t launch_quant_mxfp8(const void* x, long long rows, int K, uint8_t* codes, uint8_t* scales,
-                              hipStream_t s);
+                              bool grouped, hipStream_t s);
 hipError_t launch_gemm_a8(const GemmProblem& p, bool swiglu, hipStream_t s);
 
 // fp32 activations and weights: straightforward VALU kernels.

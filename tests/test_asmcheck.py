@@ -18,6 +18,8 @@ _Zkernel:
 \t;;#ASMSTART
 \tv_mfma_f32_32x32x16_bf16 a[16:31], v[2:5], v[6:9], a[16:31]
 \ts_nop 7
+\ts_nop 7
+\ts_nop 7
 \t;;#ASMEND
 \tv_accvgpr_read_b32 v11, a17
 \t;;#ASMSTART
@@ -26,19 +28,29 @@ _Zkernel:
 \t;;#ASMEND
 \tv_add_u32_e32 v50, 1, v51
 \tscratch_store_dwordx4 off, v[44:47], off
+\t;;#ASMSTART
+\tv_mfma_scale_f32_32x32x64_f8f6f4 v[64:79], v[2:9], v[10:13], v[64:79], v14, v15 blgp:4
+\tds_read_b32 v16, v17 offset:256
+\ts_waitcnt lgkmcnt(0)
+\t;;#ASMEND
+\tv_mov_b32_e32 v80, v79
 """
 
 
 def test_checker_flags_reads_right_after_mfma_blocks():
     found = asmcheck.find_hazards(SNIPPET)
-    # block 1: a3 read at once; block 2: padded by s_nop, fine; block 3: the
-    # spill of v[44:47] within the window
-    assert len(found) == 2
-    assert "a3" in found[0] and "v[44:47]" in found[1]
+    # block 1: a3 read at once; block 2: padded by 24 wait states, fine;
+    # block 3: the spill of v[44:47] within the window; block 4: an LDS read
+    # after the MFMA is no padding, and v79 is read right after the block
+    assert len(found) == 3
+    assert "a3" in found[0] and "v[44:47]" in found[1] and "v79" in found[2]
 
 
 @pytest.mark.skipif(not os.path.exists(asmcheck.HIPCC) and shutil.which("hipcc") is None,
                     reason="hipcc not available")
-def test_gemm_kernels_have_no_mfma_result_hazards():
-    src = os.path.join(os.path.dirname(asmcheck.__file__), "csrc", "gemm.hip")
-    assert asmcheck.find_hazards(asmcheck.compile_to_asm(src)) == []
+@pytest.mark.parametrize("name", asmcheck.SOURCES)
+def test_gemm_kernels_have_no_mfma_result_hazards(name):
+    src = os.path.join(os.path.dirname(asmcheck.__file__), "csrc", name)
+    asm = asmcheck.compile_to_asm(src)
+    assert "v_mfma" in asm
+    assert asmcheck.find_hazards(asm) == []

@@ -99,7 +99,10 @@ def test_a8_gate_up_H_against_oracle():
     rows = cfg.T * cfg.k
     hb = got["H"].reshape(-1).view(np.uint8)
     hc = hb[:rows * cfg.F].reshape(rows, cfg.F)[:A]
-    hs = hb[rows * cfg.F:rows * cfg.F + rows * cfg.F // 32].reshape(rows, cfg.F // 32)[:A]
+    # scales: grouped, [ceil(F/512)][rows][16]
+    G = (cfg.F + 511) // 512
+    grouped = hb[rows * cfg.F:rows * cfg.F + G * rows * 16].reshape(G, rows, 16)
+    hs = grouped.transpose(1, 0, 2).reshape(rows, G * 16)[:A, :cfg.F // 32]
     tab = _e4m3_table()
     h_gpu = tab[hc] * np.repeat(2.0 ** (hs.astype(np.float64) - 127), 32, axis=1)
     h_ref = np.empty((A, cfg.F))
