@@ -41,10 +41,11 @@
  *   slot_pos int32 [T][k]   row of (t, j) in the segments, -1 if dropped
  *   perm_token int32 [T*k]  token of each segment row (rows < A written)
  *   x_perm   [T*k][D] act dtype  H [T*k][F] act dtype  y_perm [T*k][D] fp32
- *   (MOE_MXFP4_A8: H holds MXFP8, e4m3 codes uint8 [T*k][F] followed by
- *   e8m0 scales uint8 [ceil(F/512)][T*k][16] -- the scale of row r, block
- *   b at ((b/16)*T*k + r)*16 + b%16, so that 8 GEMM steps of a row's
- *   scales are one 16-byte piece -- in the same [T*k][F] bf16-sized buffer)
+ *   (MOE_MXFP4_A8: x_perm and H hold MXFP8 rows, e4m3 codes uint8
+ *   [T*k][W] (W = D for x_perm, F for H) followed by e8m0 scales uint8
+ *   [ceil(W/512)][T*k][16] -- the scale of row r, block b at
+ *   ((b/16)*T*k + r)*16 + b%16, so that 8 GEMM steps of a row's scales are
+ *   one 16-byte piece -- in the same bf16-sized buffers)
  *   y        [T][D]   act dtype
  * Every device pointer must be 16-byte aligned.
  *
@@ -134,8 +135,7 @@ typedef struct moe_weights {
  * MOE_WS_DISPATCH for moe_dispatch (per-chunk expert counts),
  * MOE_WS_EXPERT_FFN for moe_expert_ffn / _gate_up / _down (the device tile
  * map and, with bf16 activations, 64 MiB of fp32 partial sums plus ready
- * flags for the GEMM tiles that are split along K; with MOE_MXFP4_A8 also
- * the MXFP8 copy of x_perm), MOE_WS_FORWARD for
+ * flags for the GEMM tiles that are split along K), MOE_WS_FORWARD for
  * moe_forward (all of the above plus H, y_perm, x_perm for fp32
  * activations only, the MXFP8 copy of x for MOE_MXFP4_A8 and, with a
  * shared expert, its H and output). A workspace carries state only within
@@ -159,7 +159,8 @@ int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* 
  * step 3 GetTokensForExpert/Gather, pitfall 1). Groups the (t, j) pairs by
  * expert, token order inside each expert; pairs whose rank within their
  * expert reaches cfg->capacity are dropped. Writes counts, offsets,
- * slot_pos, perm_token and copies each kept pair's x row to x_perm.
+ * slot_pos, perm_token and copies each kept pair's x row to x_perm (with
+ * MOE_MXFP4_A8: the row's MXFP8 quantisation, quantised once per token).
  * Integer outputs are deterministic and bit-exact. */
 int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
                  int32_t* offsets, int32_t* slot_pos, int32_t* perm_token, void* x_perm,
@@ -170,8 +171,8 @@ int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int
  * for every kept row r of expert e's segment,
  *   H[r] = SiLU(clampL(x_perm[r] W_gate[e])) * clampL(x_perm[r] W_up[e])
  *          (rounded to the act dtype), y_perm[r] = H[r] W_down[e] (fp32).
- * With MOE_MXFP4_A8 the products read the MXFP8 values of x_perm[r] and of
- * H[r] (H computed in fp32, then stored as MXFP8).
+ * With MOE_MXFP4_A8, x_perm is the MXFP8 x_perm that moe_dispatch writes
+ * and H is stored as MXFP8 (computed in fp32, then quantised).
  * Rows r >= offsets[E] are not written. */
 int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
                    const moe_weights* w, void* H, float* y_perm, void* ws, size_t ws_bytes,

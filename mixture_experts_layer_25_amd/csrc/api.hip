@@ -99,14 +99,6 @@ size_t ffn_ws(const moe_cfg& c) { return tilemap_bytes(c) + moe::split_bytes(c);
 size_t mxfp8_bytes(size_t rows, int K) {
   return moe::align_up(rows * K, kAlign) + moe::align_up((size_t)((K + 511) / 512) * rows * 16, kAlign);
 }
-// the stage entry points' FFN workspace: with MXFP8 activations, the
-// quantised x_perm follows the tile map and split slots
-size_t ffn_stage_ws(const moe_cfg& c) {
-  return ffn_ws(c) + (is_a8(c) ? mxfp8_bytes((size_t)c.T * c.top_k, c.D) : 0);
-}
-uint8_t* stage_xq(const moe_cfg& c, void* ws) {
-  return is_a8(c) ? static_cast<uint8_t*>(ws) + ffn_ws(c) : nullptr;
-}
 int32_t* split_flags_of(const moe_cfg& c, int32_t* tilemap) {
   if (!moe::gemm_splits(c)) return nullptr;
   return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tilemap) + tilemap_bytes(c));
@@ -164,9 +156,10 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
 
 // gate + up with the SwiGLU epilogue -> H
 // (gather: nullptr, x_perm holds the dispatched rows; else x_perm is x and
-// routed row r reads row gather[r] of it). With MXFP8 activations the A
-// rows are first quantised into xq (codes, then scales) and H is written
-// as MXFP8 (codes [T*k][F], then scales [T*k][F/32]).
+// routed row r reads row gather[r] of it). With MXFP8 activations H is
+// written as MXFP8 (codes [T*k][F], then grouped scales); the dispatched
+// x_perm is MXFP8 already (codes [T*k][D], then grouped scales), and x
+// (gathered) is first quantised into xq.
 hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gather,
                        const int32_t* offsets, const moe_weights& w, void* H, int32_t* tilemap,
                        uint8_t* xq, hipStream_t s) {
@@ -188,12 +181,15 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gath
   g.S1 = w.S_up;
   g.out = H;
   if (!is_a8(c)) return moe::launch_gemm_swiglu(g, s);
-  const long long qrows = gather ? c.T : (long long)c.T * c.top_k;
-  uint8_t* xs = xq + moe::align_up((size_t)qrows * c.D, kAlign);
-  e = moe::launch_quant_mxfp8(x_perm, qrows, c.D, xq, xs, true, s);
-  if (e != hipSuccess) return e;
-  g.A = xq;
-  g.SA = xs;
+  if (gather) {
+    uint8_t* xs = xq + moe::align_up((size_t)c.T * c.D, kAlign);
+    e = moe::launch_quant_mxfp8(x_perm, c.T, c.D, xq, xs, true, s);
+    if (e != hipSuccess) return e;
+    g.A = xq;
+    g.SA = xs;
+  } else {
+    g.SA = static_cast<const uint8_t*>(x_perm) + (size_t)g.rows * c.D;  // scales after codes
+  }
   return moe::launch_gemm_a8(g, true, s);
 }
 
@@ -280,7 +276,7 @@ int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes) {
   if (!bytes) return MOE_ERR_INVALID_ARG;
   switch (kind) {
     case MOE_WS_DISPATCH: *bytes = dispatch_ws(*cfg); return MOE_OK;
-    case MOE_WS_EXPERT_FFN: *bytes = cfg->act_dtype == MOE_F32 ? 0 : ffn_stage_ws(*cfg); return MOE_OK;
+    case MOE_WS_EXPERT_FFN: *bytes = cfg->act_dtype == MOE_F32 ? 0 : ffn_ws(*cfg); return MOE_OK;
     case MOE_WS_FORWARD: *bytes = carve_forward(*cfg, nullptr).bytes; return MOE_OK;
     default: return MOE_ERR_INVALID_ARG;
   }
@@ -321,11 +317,11 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offset
   if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
   if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(H) || !dev_ok(y_perm))
     return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_stage_ws(*cfg)))
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_expert_ffn(*cfg, x_perm, nullptr, offsets, *w, H, y_perm,
-                                   static_cast<int32_t*>(ws), stage_xq(*cfg, ws),
+                                   static_cast<int32_t*>(ws), nullptr,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -335,11 +331,11 @@ int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* of
   if (st != MOE_OK) return st;
   if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
   if (!dev_ok(x_perm) || !dev_ok(offsets) || !dev_ok(H)) return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_stage_ws(*cfg)))
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_gate_up(*cfg, x_perm, nullptr, offsets, *w, H, static_cast<int32_t*>(ws),
-                                stage_xq(*cfg, ws), static_cast<hipStream_t>(stream)));
+                                nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
@@ -348,7 +344,7 @@ int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
   if (st != MOE_OK) return st;
   if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
   if (!dev_ok(H) || !dev_ok(offsets) || !dev_ok(y_perm)) return MOE_ERR_INVALID_ARG;
-  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_stage_ws(*cfg)))
+  if (cfg->act_dtype != MOE_F32 && (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)))
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_down(*cfg, H, offsets, *w, y_perm, static_cast<int32_t*>(ws), true,

@@ -19,9 +19,13 @@
 //          waves' counts + earlier pairs in the wave (per-expert lane masks
 //          in LDS) -> slot_pos, perm_token;
 //   copy:  one wave per token reads the row once (16-byte vectors) and
-//          writes it to each kept slot.
+//          writes it to each kept slot. With MXFP8 activation operands
+//          (MOE_MXFP4_A8) the wave quantises the row once instead and writes
+//          the codes to each kept slot's row, the scales in the grouped
+//          layout of the A8 GEMM after the codes.
 #include "common.h"
 #include "launch.h"
+#include "mxfp8.h"
 
 namespace moe {
 namespace {
@@ -195,6 +199,43 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
   }
 }
 
+__global__ __launch_bounds__(256) void dispatch_copy_mxfp8_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ slot_pos, int T, int k, int D,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int pos[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
+  const long long rows = (long long)T * k;
+  const int KB = D / 32;
+  for (int b = lane; b < KB; b += 64) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * D + 32 * b);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = src[i];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[8 * i + 2 * c] = __uint_as_float(ww[c] << 16);
+        v[8 * i + 2 * c + 1] = __uint_as_float(ww[c] & 0xFFFF0000u);
+      }
+    }
+    uint32_t q[8];
+    const uint32_t s = mxfp8_block(v, q);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (pos[j] < 0) continue;
+      uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)pos[j] * D + 32 * b);
+      dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+      dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+      scales[grouped_scale(pos[j], b, rows)] = (uint8_t)s;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, int32_t* counts,
@@ -206,6 +247,13 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
   dispatch_rank_kernel<<<nchunks, 256, 0, s>>>(idx, counts, chunk_ws, c.T, c.E, c.top_k,
                                                c.capacity, nchunks, offsets, slot_pos, perm);
   if (!x_perm) return hipGetLastError();  // the caller gathers rows through perm
+  if (c.w_dtype == MOE_MXFP4_A8) {
+    uint8_t* q = static_cast<uint8_t*>(x_perm);
+    dispatch_copy_mxfp8_kernel<<<ceil_div(c.T, 4), 256, 0, s>>>(
+        static_cast<const uint16_t*>(x), slot_pos, c.T, c.top_k, c.D, q,
+        q + (size_t)c.T * c.top_k * c.D);
+    return hipGetLastError();
+  }
   const size_t row_bytes = (size_t)c.D * (c.act_dtype == MOE_BF16 ? 2 : 4);
   dispatch_copy_kernel<<<ceil_div(c.T, 4), 256, 0, s>>>(
       static_cast<const uint4*>(x), slot_pos, c.T, c.top_k, static_cast<int>(row_bytes / 16),

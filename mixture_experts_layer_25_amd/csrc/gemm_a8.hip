@@ -46,6 +46,7 @@
 // it as MXFP8 (each wave's 32 f-columns of a row are one block: codes
 // [rows][F] and scales [rows][F/32]); down stores fp32 rows.
 #include "gemm_tile.h"
+#include "mxfp8.h"
 
 namespace moe {
 namespace {
@@ -65,14 +66,6 @@ static_assert(LDS8 >= 8 * 128 * 128, "the epilogue stages 16 KB per wave");
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Byte offset of the e8m0 scale of (row, 32-element block kb) in the
-// grouped scale layout the GEMM reads: [ceil(K/512)][rows][16], i.e. for
-// each run of 16 blocks (8 GEMM steps) every row's 16 scales are one
-// 16-byte piece, copied by one lane.
-__device__ __forceinline__ size_t grouped_scale(long long row, int kb, long long rows) {
-  return ((size_t)(kb / 16) * rows + row) * 16 + kb % 16;
-}
 
 __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 4, 0, 0);
@@ -103,37 +96,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // the two 16-byte halves of an MFMA A operand as one 8-register value
 __device__ __forceinline__ i32x8_t join8(i32x4_t lo, i32x4_t hi) {
   return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// Two floats -> two e4m3 codes in the low (HI = false) or high 16 bits of
-// `old`, saturated to +-448, rounded to nearest even.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2(float a, float b, uint32_t old) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
-}
-
-// MXFP8 block of 32 fp32 values: returns the e8m0 scale code and writes the
-// 32 e4m3 codes (8 dwords, element 4i + b in byte b of dword i).
-__device__ __forceinline__ uint32_t mxfp8_block(const float (&v)[32], uint32_t (&q)[8]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // floor(log2 amax) = biased exponent field - 127 for normal amax; zero
-  // and subnormal amax take the lowest scale code, 0
-  const int ef = (int)(__float_as_uint(amax) >> 23);
-  const int s = max(ef - 8, 0);  // scale code = floor(log2 amax) - 8 + 127
-  const int sh = 127 - s;        // elements are v * 2^sh
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = __builtin_amdgcn_ldexpf(v[4 * i], sh);
-    const float b = __builtin_amdgcn_ldexpf(v[4 * i + 1], sh);
-    const float c = __builtin_amdgcn_ldexpf(v[4 * i + 2], sh);
-    const float d = __builtin_amdgcn_ldexpf(v[4 * i + 3], sh);
-    q[i] = fp8x2<true>(c, d, fp8x2<false>(a, b, 0u));
-  }
-  return (uint32_t)s;
 }
 
 template <bool GROUPED>
@@ -305,11 +267,12 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
 #define A8_MF(I, J, AR, BR, SA, SB)                                                  \
   "v_mfma_scale_f32_32x32x64_f8f6f4 %[c" #I #J "], %[" AR "], %[" BR "], %[c" #I #J   \
   "], %[" SA "], %[" SB "] op_sel_hi:[0,0,0] blgp:4\n\t"
-  // MFMAs of tiles I0, I1 (A operands a0, a1; scales s0, s1) on B b0, b1
-  // (scales t0, t1), with the reads R0..R3 between them and R4 after them
+  // MFMAs of tiles I0, I1 (A operands a0, a1; scales s0, s1) on B b0 then
+  // b1 (scales t0, t1): R0 before them, R1 after the first, R2 after the
+  // second (the last use of b0), R3 after the third, R4 after the fourth
 #define A8_HALF(I0, I1, R0, R1, R2, R3, R4)                                          \
-  A8_MF(I0, 0, "a0", "b0", "s0", "t0") R0 A8_MF(I0, 1, "a0", "b1", "s0", "t1") R1      \
-  A8_MF(I1, 0, "a1", "b0", "s1", "t0") R2 A8_MF(I1, 1, "a1", "b1", "s1", "t1") R3 R4
+  R0 A8_MF(I0, 0, "a0", "b0", "s0", "t0") R1 A8_MF(I1, 0, "a1", "b0", "s1", "t0") R2    \
+  A8_MF(I0, 1, "a0", "b1", "s0", "t1") R3 A8_MF(I1, 1, "a1", "b1", "s1", "t1") R4
 #define A8_HALF_X(...) A8_HALF(__VA_ARGS__)  // expands a read list into R0..R4
   // read OUT (16 or 4 bytes) at lane base ADDR + stage offset (register so)
   // + OFF, forming the address in register TMP
@@ -320,18 +283,22 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
 #define A8_RB(OUT, ADDR, OREG, OFF, TMP)                                             \
   "v_add_u32 %[" TMP "], %[" OREG "], %[" ADDR "]\n\t"                               \
   "ds_read_u8 %[" OUT "], %[" TMP "] offset:" OFF "\n\t"
-  // Q of this step (A rows 64.., their scales 1024..)
+  // first half: this step's second B fragment and its scale (b1, t1: the
+  // oldest reads, needed by the third MFMA), then Q of this step (A rows
+  // 64.., their scales 1024..)
 #define A8_RQ                                                                        \
-  A8_R("nl0", "alo", "4096", "u0") A8_R("ng0", "ahi", "4096", "u1"),                 \
-      A8_R("nl1", "alo", "6144", "u0") A8_R("ng1", "ahi", "6144", "u1"),             \
-      A8_RB("ns0", "as", "ao", "1024", "u0"), A8_RB("ns1", "as", "ao", "1536", "u1"), ""
-  // P of the next step, then (after the last MFMA) its B fragments and scales
+  A8_R("b1", "bc1", "0", "u0") A8_RB("t1", "bs1", "so", "0", "u1"),                  \
+      A8_R("nl0", "alo", "4096", "u0") A8_R("ng0", "ahi", "4096", "u1")              \
+      A8_R("nl1", "alo", "6144", "u0") A8_R("ng1", "ahi", "6144", "u1")              \
+      A8_RB("ns0", "as", "ao", "1024", "u0") A8_RB("ns1", "as", "ao", "1536", "u1"),  \
+      "s_waitcnt lgkmcnt(6)\n\t", "", ""
+  // second half: P of the next step, then (after the last use of b0) its
+  // first B fragment and scale; its b1, t1 are read by its first half
 #define A8_RP                                                                        \
-  A8_R("nl0", "alo", "0", "u0") A8_R("ng0", "ahi", "0", "u1"),                       \
-      A8_R("nl1", "alo", "2048", "u0") A8_R("ng1", "ahi", "2048", "u1"),             \
-      A8_RB("ns0", "as", "ao", "0", "u0"), A8_RB("ns1", "as", "ao", "512", "u1"),    \
-      A8_R("b0", "bc0", "0", "u0") A8_R("b1", "bc1", "0", "u1")                      \
-      A8_RB("t0", "bs0", "so", "0", "u0") A8_RB("t1", "bs1", "so", "0", "u1")
+  "", A8_R("nl0", "alo", "0", "u0") A8_R("ng0", "ahi", "0", "u1")                    \
+      A8_R("nl1", "alo", "2048", "u0") A8_R("ng1", "ahi", "2048", "u1")              \
+      A8_RB("ns0", "as", "ao", "0", "u0") A8_RB("ns1", "as", "ao", "512", "u1"),     \
+      A8_R("b0", "bc0", "0", "u0") A8_RB("t0", "bs0", "so", "0", "u1"), "", ""
 #define A8_BASES                                                                     \
   [alo] "v"(a_lo), [ahi] "v"(a_hi), [bc0] "v"(bc_a[0]), [bc1] "v"(bc_a[1]),          \
       [as] "v"(as_a), [bs0] "v"(bs_a[0]), [bs1] "v"(bs_a[1])
@@ -346,10 +313,10 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
   asm volatile("s_nop 4\n\t" A8_HALF_X(0, 1, A8_RQ) "s_waitcnt lgkmcnt(0)"           \
                : [nl0] "=&v"(ql0), [ng0] "=&v"(qg0), [nl1] "=&v"(ql1), [ng1] "=&v"(qg1), \
                  [ns0] "=&v"(sa2), [ns1] "=&v"(sa3), [u0] "=&v"(u0), [u1] "=&v"(u1),  \
-                 A8_ACC                                                              \
+                 [b1] "=&v"(b1), [t1] "=&v"(t1), A8_ACC                              \
                : [a0] "v"(join8(pl0, pg0)), [a1] "v"(join8(pl1, pg1)), [b0] "v"(b0),  \
-                 [b1] "v"(b1), [s0] "v"(sa0), [s1] "v"(sa1), [t0] "v"(t0), [t1] "v"(t1), \
-                 [so] "s"(SO), [ao] "s"(AO), A8_BASES                                \
+                 [s0] "v"(sa0), [s1] "v"(sa1), [t0] "v"(t0), [so] "s"(SO), [ao] "s"(AO), \
+                 A8_BASES                                                            \
                : "memory")
   // second half: tiles 2, 3 from Q; reads P, B and B scales of the next
   // step (stage offset SO, A-scale offset AO)
@@ -357,9 +324,10 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
   asm volatile("s_nop 4\n\t" A8_HALF_X(2, 3, A8_RP) "s_waitcnt lgkmcnt(0)"           \
                : [nl0] "=&v"(pl0), [ng0] "=&v"(pg0), [nl1] "=&v"(pl1), [ng1] "=&v"(pg1), \
                  [ns0] "=&v"(sa0), [ns1] "=&v"(sa1), [u0] "=&v"(u0), [u1] "=&v"(u1),  \
-                 [b0] "+v"(b0), [b1] "+v"(b1), [t0] "+v"(t0), [t1] "+v"(t1), A8_ACC   \
-               : [a0] "v"(join8(ql0, qg0)), [a1] "v"(join8(ql1, qg1)), [s0] "v"(sa2), \
-                 [s1] "v"(sa3), [so] "s"(SO), [ao] "s"(AO), A8_BASES                 \
+                 [b0] "+v"(b0), [t0] "+v"(t0), A8_ACC                                \
+               : [a0] "v"(join8(ql0, qg0)), [a1] "v"(join8(ql1, qg1)), [b1] "v"(b1),  \
+                 [s0] "v"(sa2), [s1] "v"(sa3), [t1] "v"(t1), [so] "s"(SO), [ao] "s"(AO), \
+                 A8_BASES                                                            \
                : "memory")
 #define A8_H2_LAST()                                                                 \
   asm volatile("s_nop 4\n\t" A8_HALF(2, 3, "", "", "", "", "") MFMA_TAIL             \
@@ -413,13 +381,12 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
     // step 0's P, B and scales
     asm volatile(A8_R("nl0", "alo", "0", "u0") A8_R("ng0", "ahi", "0", "u1")
                  A8_R("nl1", "alo", "2048", "u0") A8_R("ng1", "ahi", "2048", "u1")
-                 A8_R("nb0", "bc0", "0", "u0") A8_R("nb1", "bc1", "0", "u1")
-                 A8_RB("ns0", "as", "ao", "0", "u0") A8_RB("ns1", "as", "ao", "512", "u1")
-                 A8_RB("nt0", "bs0", "so", "0", "u0") A8_RB("nt1", "bs1", "so", "0", "u1")
+                 A8_R("nb0", "bc0", "0", "u0") A8_RB("ns0", "as", "ao", "0", "u1")
+                 A8_RB("ns1", "as", "ao", "512", "u0") A8_RB("nt0", "bs0", "so", "0", "u1")
                  "s_waitcnt lgkmcnt(0)"
                  : [nl0] "=&v"(pl0), [ng0] "=&v"(pg0), [nl1] "=&v"(pl1), [ng1] "=&v"(pg1),
-                   [nb0] "=&v"(b0), [nb1] "=&v"(b1), [ns0] "=&v"(sa0), [ns1] "=&v"(sa1),
-                   [nt0] "=&v"(t0), [nt1] "=&v"(t1), [u0] "=&v"(u0), [u1] "=&v"(u1)
+                   [nb0] "=&v"(b0), [ns0] "=&v"(sa0), [ns1] "=&v"(sa1), [nt0] "=&v"(t0),
+                   [u0] "=&v"(u0), [u1] "=&v"(u1)
                  : [so] "s"(0u), [ao] "s"(as_off(kt_begin)), A8_BASES
                  : "memory");
     for (; kt + 1 < nk; ++kt) {

@@ -45,8 +45,21 @@ def test_small_stagewise(name):
     got = gpu_forward(inp, stagewise=True)
     check_routing(cfg, got, ref)
     A = int(ref["offsets"][-1])
-    # x_perm rows are the byte-exact x rows of perm_token
-    assert np.array_equal(got["x_perm"][:A], inp.x[ref["perm"][:A]])
+    if cfg.wdt == syn.MXFP4_A8:
+        # x_perm rows are the MXFP8 quantisation of the x rows of perm_token:
+        # codes [T*k][D], then scales grouped as [ceil(D/512)][T*k][16]
+        rows, D = cfg.T * cfg.k, cfg.D
+        xb = got["x_perm"].reshape(-1).view(np.uint8)
+        codes = xb[:rows * D].reshape(rows, D)[:A]
+        G = (D + 511) // 512
+        sc = xb[rows * D:rows * D + G * rows * 16].reshape(G, rows, 16)
+        sc = sc.transpose(1, 0, 2).reshape(rows, G * 16)[:A, :D // 32]
+        rc, rs = oracle.mxfp8_quantize(act_to_f64(inp.x[ref["perm"][:A]]))
+        assert np.array_equal(sc, rs)
+        assert np.array_equal(np.where(codes == 0x80, 0, codes), np.where(rc == 0x80, 0, rc))
+    else:
+        # x_perm rows are the byte-exact x rows of perm_token
+        assert np.array_equal(got["x_perm"][:A], inp.x[ref["perm"][:A]])
     err = assert_close(got["y"], ref["y"], tol_for(cfg), f"{name} y")
     print(f"[parity] {name}: max rel err {err:.3g}", flush=True)
 
