@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -93,8 +94,30 @@ def roofline_kernel(cfg):
     return {"name": "gemm_kernel<0, false>", "src": "gemm.hip", "bound": "mfma"}
 
 
+def _sources_of(name, seen=None):
+    """The kernel source and the local headers it includes, recursively."""
+    seen = [] if seen is None else seen
+    if name in seen or not os.path.exists(os.path.join(CSRC, name)):
+        return seen
+    seen.append(name)
+    for inc in re.findall(r'^#include "([^"/]+)"', open(os.path.join(CSRC, name)).read(), re.M):
+        _sources_of(inc, seen)
+    return seen
+
+
 def src_sha256(name):
-    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
+    """sha256 of the code that builds the kernel: its source and the local
+    headers it includes, with // comments and blank lines removed (a change
+    of comments does not change the kernel; a change of code anywhere in
+    those files does)."""
+    h = hashlib.sha256()
+    for f in sorted(_sources_of(name)):
+        h.update(f.encode())
+        for line in open(os.path.join(CSRC, f)).read().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 def short_name(n):
@@ -176,7 +199,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, command):
              f"# command: {command}",
              f"# scaling: FETCH_SIZE x {f['scale']:.4f} (copy of 256 MiB read {f['copy_kib']:.1f} KiB), "
              f"WRITE_SIZE x {w['scale']:.4f} (copy wrote {w['copy_kib']:.1f} KiB)",
-             f"# source sha256 of {rk['src']}: {rec['kernel_src_sha256']}",
+             f"# code sha256 of {rk['src']} and its headers (comments stripped): "
+             f"{rec['kernel_src_sha256']}",
              f"{'kernel':90s} {'fetch_KiB':>12s} {'write_KiB':>12s} {'scaled_MB':>10s}"]
     for k, b in rec["per_kernel_bytes"].items():
         lines.append(f"{k:90s} {f['kib_per_dispatch'].get(k, 0.0):12.1f} "

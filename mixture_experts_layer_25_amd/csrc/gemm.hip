@@ -7,8 +7,9 @@
 // clamped to [-L, L] before SiLU(gate)*up; routed experts may be FP4
 // (here MXFP4: e2m1 codes with an e8m0 scale per 32 K-elements).
 //
-// One kernel, gemm_kernel<MODE, MX>, for bf16 weights (MX = false) and
-// MXFP4 weights (MX = true).
+// One kernel, gemm_kernel<MODE, MX>, for bf16 activations with bf16
+// weights (MX = false) or MXFP4 weights (MX = true); MXFP8 activations with
+// MXFP4 weights run on the block-scaled MFMA in gemm_a8.hip.
 //
 // Tile: 256 rows x 256 B-columns, 32 k per step, 512 threads (8 waves, two
 // per SIMD). SwiGLU: the 256 B-columns are 128 gate and the same 128 up
@@ -59,7 +60,7 @@
 // while the MFMA pipe is busy anyway; issued between the blocks, the copies
 // cost a fifth more cycles per step.
 //
-// Tile schedule (schedule_tile): the real tiles, in expert_tile_of order,
+// Tile schedule (schedule_tile, gemm_tile.h): the real tiles, in expert_tile_of order,
 // are cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD
 // b mod 8). Whole rounds of 32 tiles (one per CU of the XCD) run as whole
 // tiles; the tiles of the last, partial round are split along K so that

@@ -39,12 +39,16 @@
 // scales travel in as few instructions as possible: per step and CU 16
 // instructions of A, 8 of B codes, 2 of B scales and half of one of A
 // scales, against 40 when every scale byte had a lane of its own. One
-// barrier per step. A step is two halves of 4 MFMAs (row tiles 0-1, then
-// 2-3); each half is one asm block whose LDS reads (the other half's
-// fragments) sit between its MFMAs.
+// barrier per step (a barrier every second step, with six stages, left one
+// step fewer in flight and was 13 % slower). A step is two halves of 4
+// MFMAs (row tiles 0-1, then 2-3); each half is one asm block whose LDS
+// reads (the other half's fragments) sit between its MFMAs, issued at
+// least two MFMAs before the block's final wait.
+// A rows: MXFP8 x_perm from the dispatch, H, or (fused layer) the MXFP8
+// copy of x through the gather list.
 // Epilogues: SwiGLU forms h = SiLU(clamp(g)) * clamp(u) in fp32 and writes
 // it as MXFP8 (each wave's 32 f-columns of a row are one block: codes
-// [rows][F] and scales [rows][F/32]); down stores fp32 rows.
+// [rows][F], then grouped scales); down stores fp32 rows.
 #include "gemm_tile.h"
 #include "mxfp8.h"
 
