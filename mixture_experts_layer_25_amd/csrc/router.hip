@@ -14,7 +14,9 @@
 // ALUs: a workgroup stages D-chunks of x (transposed, fp32) and of W_r in a
 // double-buffered LDS area (the next chunk's loads fly while the current one
 // is multiplied), and each thread keeps RT tokens x RE experts of
-// accumulators in registers. A token's experts live in NE adjacent lanes,
+// accumulators in registers (a lane's RE experts are adjacent, so their
+// weights arrive in one or two vector LDS reads per d, and its RT tokens'
+// x in one broadcast read). A token's experts live in NE adjacent lanes,
 // so top-k is a butterfly arg-max over those lanes, k times, with no
 // sorting.
 #include <math.h>
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(NTH) void router_kernel(RouterArgs a) {
   constexpr int VX = XBF16 ? 8 : 4;                     // x values per 16-byte load
   constexpr int NXV = (TB * DK / VX + NTH - 1) / NTH;  // x loads per thread per chunk
   constexpr int NWV = (DK * EP / 4 + NTH - 1) / NTH;   // W_r loads per thread per chunk
-  __shared__ float xs[2][DK][TB];
-  __shared__ float wsm[2][DK][EP];
+  __shared__ __attribute__((aligned(16))) float xs[2][DK][TB];
+  __shared__ __attribute__((aligned(16))) float wsm[2][DK][EP];
 
   const int tid = threadIdx.x;
   const int te = tid % NE;
@@ -233,8 +235,9 @@ __global__ __launch_bounds__(NTH) void router_kernel(RouterArgs a) {
       float xv[RT], wv[RE];
 #pragma unroll
       for (int i = 0; i < RT; ++i) xv[i] = xs[buf][dd][tt * RT + i];
+      // the lane's RE experts are adjacent: one or two vector LDS reads
 #pragma unroll
-      for (int j = 0; j < RE; ++j) wv[j] = wsm[buf][dd][te + NE * j];
+      for (int j = 0; j < RE; ++j) wv[j] = wsm[buf][dd][te * RE + j];
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(NTH) void router_kernel(RouterArgs a) {
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < RE; ++j) lg[(tt * RT + i) * EP + te + NE * j] = acc[i][j];
+    for (int j = 0; j < RE; ++j) lg[(tt * RT + i) * EP + te * RE + j] = acc[i][j];
   __syncthreads();
 
   select_topk<NE, RE, RT>(a, lg, tt, te, t0);
