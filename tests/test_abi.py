@@ -47,6 +47,9 @@ def _cfg(**kw):
     (dict(E=64, top_k=17), -2), (dict(act="f32", w="bf16"), -1), (dict(act="bf16", w="f32"), -1),
     (dict(D=4104), -2), (dict(shared_F=1000), -2), (dict(T=-1), -1),
     (dict(act="f32", w="f32", shared_F=64), -2), (dict(clamp=float("inf")), -1),
+    # MXFP8 activations: bf16 activations only, D and F multiples of 64
+    (dict(act="f32", w="mxfp4_a8"), -1), (dict(w="mxfp4_a8", D=4128), -2),
+    (dict(w="mxfp4_a8", F=14368), -2),
 ])
 def test_invalid_configs_rejected(kw, status):
     c = _cfg(**kw)
@@ -77,10 +80,27 @@ def test_null_and_misaligned_pointers_rejected():
     assert L.moe_shared_expert(ctypes.byref(cs), fake, ctypes.byref(w), fake, fake, None) == -1
 
 
+def test_quantize_mxfp8_rejects_bad_arguments():
+    L = moe.lib()
+    fake = 1 << 40  # never dereferenced: validation fails first
+    assert L.moe_quantize_mxfp8(fake, 4, 48, fake, fake, None) == -1      # K not a multiple of 32
+    assert L.moe_quantize_mxfp8(fake, 4, 0, fake, fake, None) == -1
+    assert L.moe_quantize_mxfp8(fake, -1, 64, fake, fake, None) == -1
+    assert L.moe_quantize_mxfp8(None, 4, 64, fake, fake, None) == -1
+    assert L.moe_quantize_mxfp8(fake, 4, 64, fake + 8, fake, None) == -1  # misaligned
+    assert L.moe_quantize_mxfp8(fake, 0, 64, fake, fake, None) == 0       # nothing to do
+
+
 def test_workspace_sizes_cover_the_buffers():
     c = _cfg()
-    tk = 4096 * 2
-    need = tk * 4096 * 2 + tk * 14336 * 2 + tk * 4096 * 4  # x_perm, H, y_perm
+    T, D, F, tk = 4096, 4096, 14336, 4096 * 2
+    need = tk * F * 2 + tk * D * 4  # H, y_perm (the fused layer gathers x: no x_perm)
     assert moe.workspace_size(c, moe.WS_FORWARD) >= need
+    # MXFP8 activations: also the MXFP8 copy of x (codes, grouped scales)
+    a8 = _cfg(w="mxfp4_a8")
+    assert moe.workspace_size(a8, moe.WS_FORWARD) >= need + T * D + (D // 512) * T * 16
+    # fp32 activations keep x_perm
+    f32 = _cfg(act="f32", w="f32")
+    assert moe.workspace_size(f32, moe.WS_FORWARD) >= tk * D * 4 + tk * F * 4 + tk * D * 4
     assert moe.workspace_size(c, moe.WS_DISPATCH) >= 8 * 16 * 4
     assert moe.workspace_size(c, moe.WS_EXPERT_FFN) >= 4 * (1 + 2 * (tk // 128 + 8))

@@ -19,6 +19,7 @@ CASES = {
     "mixtral_small": syn.small_variant(syn.CONFIGS["mixtral"], T=300, D=256, F=352),
     "fine384_small": syn.small_variant(syn.CONFIGS["fine384_mxfp4"], T=200, D=256, F=128),
     "capacity_small": syn.small_variant(syn.CONFIGS["capacity"], T=500, D=256, F=160),
+    "fine384_a8_small": syn.small_variant(syn.CONFIGS["fine384_mxfp4_a8"], T=200, D=256, F=128),
     # full Mixtral shape: the down GEMM's last round is split 4 ways
     "mixtral": syn.CONFIGS["mixtral"],
 }
