@@ -165,6 +165,9 @@ def route(cfg: Cfg, x, W_r, bias=None, topk_idx=None, topk_w=None, logits=None,
 
 
 def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None):
+    """moe_dispatch. x_perm is allocated in the activation dtype, [T*k, D];
+    with MXFP4_A8 weights its bytes hold MXFP8 rows (codes, then grouped
+    scales; see include/moe.h)."""
     dev = x.device
     tk = cfg.T * cfg.top_k
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
@@ -182,6 +185,8 @@ def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None):
 
 def expert_ffn(cfg: Cfg, x_perm, offsets, weights: Weights, H=None, y_perm=None, ws=None,
                stream=None):
+    """moe_expert_ffn. H is allocated in the activation dtype, [T*k, F]; with
+    MXFP4_A8 weights its bytes hold MXFP8 rows like x_perm."""
     dev = x_perm.device
     rows = max(cfg.T * cfg.top_k, 1)
     if H is None:
