@@ -11,6 +11,7 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   gate_weights    pinned: worked sqrt-softplus example, softplus tails,
                   softmax sums, renorm sums, the two top-k orderings
   dispatch        pinned: invariants, capacity 1228, brute-force segments
+  double_to_bf16  pinned: all 2^32 fp32 patterns against torch's conversion
   expert / shared pinned: E=1,k=1 SwiGLU against a numpy matmul chain,
                   clamp closed form, dense-masked brute force
   forward_tokens  pinned: dense all-experts masked brute force
@@ -76,6 +77,7 @@ def lib():
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_double_to_bf16.restype = ctypes.c_uint16
         L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_double_to_bf16_array.argtypes = [vp, ctypes.c_int64, vp]
         L.oracle_e2m1.restype = ctypes.c_double
         L.oracle_e2m1.argtypes = [ctypes.c_uint]
         L.oracle_e8m0.restype = ctypes.c_double
@@ -128,6 +130,14 @@ def bf16_to_double(b: int) -> float:
 
 def double_to_bf16(v: float) -> int:
     return lib().oracle_double_to_bf16(float(v))
+
+
+def double_to_bf16_array(v):
+    """oracle_double_to_bf16 applied to every element of a float64 array."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_double_to_bf16_array(_p(v), v.size, _p(out))
+    return out
 
 
 def e2m1(code: int) -> float:

@@ -87,6 +87,12 @@ uint16_t oracle_double_to_bf16(double v) {
   return sign | (uint16_t)((u >> 16) & 0x7FFF);
 }
 
+/* oracle_double_to_bf16 over an array (for exhaustive tests). */
+void oracle_double_to_bf16_array(const double* v, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_double_to_bf16(v[i]);
+}
+
 /* e2m1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa [OCP]. */
 double oracle_e2m1(unsigned code) {
   static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};

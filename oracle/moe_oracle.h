@@ -43,6 +43,7 @@ typedef struct {
 
 double oracle_bf16_to_double(uint16_t b);
 uint16_t oracle_double_to_bf16(double v);
+void oracle_double_to_bf16_array(const double* v, int64_t n, uint16_t* out);
 double oracle_e2m1(unsigned code);
 double oracle_e8m0(unsigned s);
 double oracle_e4m3(unsigned code);

@@ -134,6 +134,21 @@ def test_bf16_rounding_matches_torch_on_f32():
     assert bad.size == 0, [(hex(f.view(np.uint32)[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
 
 
+def test_bf16_rounding_exhaustive_over_f32():
+    """Every finite fp32 bit pattern (2^32 of them, in chunks) rounds to the
+    same bf16 as torch's float32 -> bfloat16 conversion."""
+    import torch
+    step = 1 << 26
+    for start in range(0, 1 << 32, step):
+        pats = np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)
+        f = pats.view(np.float32)
+        f = f[np.isfinite(f)]
+        ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        got = oracle.double_to_bf16_array(f.astype(np.float64))
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, [(hex(f.view(np.uint32)[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+
+
 def test_bf16_rounding_is_single_step_from_double():
     """A double just above a bf16 tie must round up; rounding through float32
     first would land on the tie and go to even."""
