@@ -55,6 +55,8 @@ def parse():
                     help="write profiles/kernel_trace_<workload>.txt from a rocprofv3 --stats run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_traffic_<workload>.{json,txt} from two --pmc runs")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="write profiles/mfma_util_<workload>.txt from a rocprofv3 --pmc MfmaUtil run")
     ap.add_argument("--profile-command", default="",
                     help="the command that produced the profile, recorded in the summary")
     ap.add_argument("--study", choices=["dense-vs-moe", "topk"],
@@ -152,6 +154,27 @@ def summarize_trace(run_dir, workload, command):
         lines.append(f"{short_name(r['Name']):90s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                      f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_mfma(run_dir, workload, command):
+    """rocprofv3 --pmc MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE
+    times the SIMD count, in per cent) -> profiles/mfma_util_<workload>.txt,
+    the mean per kernel over its dispatches."""
+    from collections import defaultdict
+    per = defaultdict(list)
+    for r in read_csv(find_one(run_dir, "counter_collection.csv")):
+        if r["Counter_Name"] == "MfmaUtil":
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    out = os.path.join(ROOT, "profiles", f"mfma_util_{workload}.txt")
+    lines = [f"# MFMA pipe utilisation per dispatch (rocprofv3 derived counter MfmaUtil = "
+             f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), per cent), workload {workload}",
+             f"# command: {command}",
+             f"{'kernel':90s} {'dispatches':>10s} {'MfmaUtil_%':>10s}"]
+    for k in sorted(per, key=lambda k: -sum(per[k]) / len(per[k])):
+        v = per[k]
+        lines.append(f"{k:90s} {len(v):10d} {sum(v) / len(v):10.1f}")
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
 
@@ -338,6 +361,8 @@ def main():
         return summarize_trace(args.summarize_trace, args.workload, args.profile_command)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.workload, args.profile_command)
+    if args.summarize_mfma:
+        return summarize_mfma(args.summarize_mfma, args.workload, args.profile_command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the layer on one GPU only (asked for --gpus {args.gpus}, "
@@ -424,7 +449,7 @@ def main():
         for i, fn in enumerate(fns):
             rc = fn()
             if rc != 0:
-                raise moe.MoEError(f"{order[i]}: status {rc}")
+                raise moe.MoEError(rc, f"{order[i]}: status {rc}")
             if evs is not None:
                 evs[i + 1].record(stream)
 
@@ -470,6 +495,25 @@ def main():
     stage_ms = {n: sum(evs[i].elapsed_time(evs[i + 1]) for evs in ev) / args.steps
                 for i, n in enumerate(order)}
     log(f"[bench] stage by stage: {stagewise_ms:.3f} ms/step")
+
+    # ---------------- memory-bound stages with the MALL flushed: before each
+    # stage a 512 MiB write (twice the 256 MB Infinity Cache) evicts what the
+    # previous stage left there; the stage is timed alone
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    nfl = min(args.steps, 10)
+    fl_ms = {n: 0.0 for n in order}
+    for _ in range(nfl):
+        for n, fn in zip(order, fns):
+            flush.zero_()
+            a0, a1 = new_event(), new_event()
+            a0.record(stream)
+            rc = fn()
+            a1.record(stream)
+            if rc != 0:
+                raise moe.MoEError(rc, f"{n}: status {rc}")
+            torch.cuda.synchronize()
+            fl_ms[n] += a0.elapsed_time(a1) / nfl
+    del flush
     work = algorithmic(cfg, A)
 
     if args.copy_calibration:
@@ -498,10 +542,14 @@ def main():
     if cfg.shared_F:
         stage_report["shared"] = {"ms": stage_ms["shared"],
                                   "TFLOP/s": tfs(work["shared_flop"], stage_ms["shared"])}
+    flushed = {n: {"ms": fl_ms[n], "GB/s": gbs(work[f"{n}_bytes"], fl_ms[n])}
+               for n in ("route", "dispatch", "combine")}
     for n in order:
         log(f"[bench] {n:9s} " + "  ".join(f"{kk} {vv:9.3f}" for kk, vv in stage_report[n].items()))
     log(f"[bench] grouped GEMM {gemm_tf:.1f} TFLOP/s = "
         f"{100 * gemm_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+    log("[bench] MALL flushed: " + "  ".join(f"{n} {v['ms']:.3f} ms {v['GB/s']:.0f} GB/s"
+                                             for n, v in flushed.items()))
 
     # Roofline of the dominant kernel: the grouped gate/up GEMM with the
     # SwiGLU epilogue. Its duration is the mean of its event intervals inside
@@ -551,6 +599,9 @@ def main():
         "grouped_gemm_tflops": gemm_tf,
         "grouped_gemm_frac_of_bf16_peak": gemm_tf / PEAK_BF16_TFLOPS,
         "stages": stage_report,
+        "stages_mall_flushed": flushed,
+        "env": {"device": torch.cuda.get_device_name(dev), "hip": torch.version.hip,
+                "torch": torch.__version__, "cus": torch.cuda.get_device_properties(dev).multi_processor_count},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
