@@ -33,7 +33,6 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc", "gemm.hip")
 
 
 def log(*a):
@@ -92,8 +91,8 @@ def roofline_kernel(cfg):
         return {"name": "gemm_a8_kernel<0>", "src": "gemm_a8.hip", "bound": "mfma",
                 "peak": PEAK_FP8_TFLOPS}
     if cfg.wdt == 2:
-        return {"name": "gemm_kernel<0, true>", "src": "gemm.hip", "bound": "mfma"}
-    return {"name": "gemm_kernel<0, false>", "src": "gemm.hip", "bound": "mfma"}
+        return {"name": "gemm_kernel<0>", "src": "gemm.hip", "bound": "mfma"}
+    return {"name": "gemm16_kernel<0>", "src": "gemm16.hip", "bound": "mfma"}
 
 
 def _sources_of(name, seen=None):

@@ -1,4 +1,5 @@
-// Grouped expert GEMMs on MFMA (bf16 in, fp32 accumulate).
+// Grouped expert GEMMs on MFMA: bf16 activations, MXFP4 weights, fp32
+// accumulate.
 //
 // "ops-transformer MoE operator on Ascend NPU", optimisation 3: every
 // expert's matmul in one launch, with a different row count per expert.
@@ -7,9 +8,10 @@
 // clamped to [-L, L] before SiLU(gate)*up; routed experts may be FP4
 // (here MXFP4: e2m1 codes with an e8m0 scale per 32 K-elements).
 //
-// One kernel, gemm_kernel<MODE, MX>, for bf16 activations with bf16
-// weights (MX = false) or MXFP4 weights (MX = true); MXFP8 activations with
-// MXFP4 weights run on the block-scaled MFMA in gemm_a8.hip.
+// gemm_kernel<MODE> takes MXFP4 weights and converts them to bf16 in
+// registers for v_mfma_f32_32x32x16_bf16. bf16 weights run on the 16x16x32
+// MFMA in gemm16.hip (same tile, copies and schedule); MXFP8 activations
+// with MXFP4 weights run on the block-scaled MFMA in gemm_a8.hip.
 //
 // Tile: 256 rows x 256 B-columns, 32 k per step, 512 threads (8 waves, two
 // per SIMD). SwiGLU: the 256 B-columns are 128 gate and the same 128 up
@@ -29,11 +31,6 @@
 //   With a gather list (the fused layer passes perm_token), routed row r
 //   is copied from row gather[r] of x: each copy lane looks its two row
 //   addresses up once per tile, so the dispatched copy of x is never built.
-//   B bf16 ([K][N], N-contiguous): k-rows of 512 bytes (32 chunks of 8
-//   columns, slot = chunk ^ 4 (k mod 4)) stored untouched; the MFMA fragment
-//   is read with the gfx950 transposing LDS load ds_read_b64_tr_b16 (within
-//   a 16-lane group, lane i receives element i of the 4 rows the group
-//   points at), two per fragment, so no transpose runs on the vector ALUs.
 //   B MXFP4 (stored by 32-k blocks, block-major, so that a step's codes of
 //   consecutive columns are consecutive 16-byte pieces; stored K-contiguous
 //   per column, every copy lane touched its own cache line and the B
@@ -46,8 +43,7 @@
 // gfx950) hit distinct bank groups (LDS bank-conflict counter: 0).
 //
 // Pipeline. Global data goes straight to LDS with global_load_lds (no
-// register staging) into a ring of stages (5 x 32 KB for bf16, 7 x 21 KB
-// for MXFP4). Each 32-k step is two half-steps of 16 k; the MFMA fragments
+// register staging) into a ring of 7 stages of 21 KB. Each 32-k step is two half-steps of 16 k; the MFMA fragments
 // of a half-step are read from LDS while the MFMAs of the previous
 // half-step run (two register sets). One barrier per two steps, in the
 // middle of every odd step kt, certifies the copies of steps kt+1 and kt+2
@@ -73,17 +69,13 @@ namespace {
 
 constexpr int BK = 32;                  // k per step
 constexpr int A_BYTES = TM * BK * 2;    // 16 KB of A per step
-constexpr int B_BYTES = TN * BK * 2;    // 16 KB of bf16 B per step
 constexpr int MXC_BYTES = TN * 16;      // 4 KB of MXFP4 codes per step
 constexpr int MXS_BYTES = TN * 4;       // 1 KB of scales (one dword each) per step
 
-template <bool MX>
-struct Stages {
-  static constexpr int bytes = MX ? A_BYTES + MXC_BYTES + MXS_BYTES : A_BYTES + B_BYTES;
-  static constexpr int count = MX ? 7 : 5;  // 147 KB / 160 KB of the 160 KB LDS
-  static constexpr int per = MX ? 3 : 4;    // copies per thread per step
-  static_assert(count >= 4, "a barrier every two steps needs four stages");
-};
+constexpr int SB = A_BYTES + MXC_BYTES + MXS_BYTES;  // one stage
+constexpr int NST = 7;                               // 147 KB of the 160 KB LDS
+constexpr int PER = 3;                               // copies per thread per step
+static_assert(NST >= 4, "a barrier every two steps needs four stages");
 
 // e2m1 code -> binary32 bits (OCP MX v1.0: bit 3 sign, 2 exponent bits with
 // bias 1, 1 mantissa bit; exponent 0 encodes 0 and 0.5).
@@ -147,10 +139,8 @@ __device__ __forceinline__ void mx_fragments(uint32_t c0, uint32_t s0, uint32_t 
 
 
 
-template <int MODE, bool MX>
+template <int MODE>
 __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
-  using St = Stages<MX>;
-  constexpr int NST = St::count, SB = St::bytes, PER = St::per;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NST * SB];
 
   const int tid = threadIdx.x;
@@ -191,36 +181,21 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     if (a.gather) arow = min((unsigned)a.gather[arow], (unsigned)(a.gather_rows - 1));
     a_g[r] = static_cast<const uint16_t*>(a.A) + (size_t)arow * K + kt_begin * BK + 8 * q;
   }
-  // ---- B copies.
-  //   bf16: LDS k-row (512 bytes = 32 chunks of 8 columns) slot c holds
-  //   chunk c ^ 4 (k mod 4); copy r of wave w fills k-rows 4w + 2r and
-  //   4w + 2r + 1 (lanes 0-31 and 32-63).
-  //   MXFP4: waves 0-3 copy the 16 code bytes of tile columns 64w + l,
-  //   waves 4-7 the scales of tile columns 64(w - 4) + l (one per lane).
-  const unsigned char* b_g[2];
-  if (!MX) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int k = 4 * wave + 2 * r + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (k & 3));
-      bool up;
-      const int col = b_column(8 * c, up);
-      const uint16_t* base = static_cast<const uint16_t*>(up ? a.B1 : a.B0);
-      b_g[r] = reinterpret_cast<const unsigned char*>(base + ((size_t)e * K + kt_begin * BK + k) * N + col);
-    }
-  } else {
+  // ---- B copies: waves 0-3 copy the 16 code bytes of tile columns
+  // 64w + l, waves 4-7 the scales of tile columns 64(w - 4) + l (one per
+  // lane). Block-major storage: step kt's codes of column col at
+  // ((e K/32 + kt) N + col) 16, its scale at (e K/32 + kt) N + col.
+  const unsigned char* b_g;
+  {
     bool up;
     const int col = b_column(64 * (wave & 3) + lane, up);
-    // block-major storage: step kt's codes of column col at
-    // ((e K/32 + kt) N + col) 16, its scale at (e K/32 + kt) N + col
     if (wave < 4) {
       const uint8_t* base = static_cast<const uint8_t*>(up ? a.B1 : a.B0);
-      b_g[0] = base + (((size_t)e * (K / 32) + kt_begin) * N + col) * 16;
+      b_g = base + (((size_t)e * (K / 32) + kt_begin) * N + col) * 16;
     } else {
       const uint8_t* base = up ? a.S1 : a.S0;
-      b_g[0] = base + ((size_t)e * (K / 32) + kt_begin) * N + col;
+      b_g = base + ((size_t)e * (K / 32) + kt_begin) * N + col;
     }
-    b_g[1] = nullptr;
   }
   auto issue_a = [&](int kt, uint32_t so) __attribute__((always_inline)) {
     unsigned char* As = smem + so;
@@ -230,15 +205,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   };
   auto issue_b = [&](int kt, uint32_t so) __attribute__((always_inline)) {
     unsigned char* Bs = smem + so + A_BYTES;
-    if (!MX) {
-      const size_t step = (size_t)kt * BK * N * 2;
-      dma16(b_g[0] + step, Bs + (4 * wave) * 512);
-      dma16(b_g[1] + step, Bs + (4 * wave + 2) * 512);
-    } else if (wave < 4) {
-      dma16(b_g[0] + (size_t)kt * N * 16, Bs + wave * 1024);
-    } else {
-      dma1(b_g[0] + (size_t)kt * N, Bs + MXC_BYTES + (wave - 4) * 256);
-    }
+    if (wave < 4) dma16(b_g + (size_t)kt * N * 16, Bs + wave * 1024);
+    else dma1(b_g + (size_t)kt * N, Bs + MXC_BYTES + (wave - 4) * 256);
   };
 
   // wave's B-column bases: j = 0 gate (or first half), j = 1 up (second)
@@ -265,10 +233,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   // Per-lane LDS byte addresses, in stage 0, of the MFMA fragments.
   //   A: row m = 128 wm + lrow, k-group 2 kk + lq (fragment i is 32 rows =
   //      2048 bytes further).
-  //   bf16 B: transposed reads of k-rows 8 lq + tr_row and 8 lq + tr_row + 4
-  //      (2048 bytes apart) of the half-step kk (kk = 1 is 16 k-rows = 8192
-  //      bytes further), for the wave's two B-column bases.
-  //   MXFP4 B: code bytes 4 lq.. of column bcol[j] + lrow (kk = 1 is 8
+  //   B: code bytes 4 lq.. of column bcol[j] + lrow (kk = 1 is 8
   //      bytes further) and that column's scale dword.
   uint32_t a_addr[2], b_addr[2], s_addr[2];
   {
@@ -276,20 +241,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       a_addr[kk] = smem_addr + m * 64 + (((2 * kk + lq) ^ swz4(m)) * 16);
-    const int tr_row = (lane & 15) >> 2;
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if (!MX) {
-        const int col = bcol[j] + tr_col;
-        const int r0 = 8 * lq + tr_row;  // r0 & 3 == tr_row
-        b_addr[j] = smem_addr + A_BYTES + r0 * 512 + ((col >> 3) ^ (4 * tr_row)) * 16 + (col & 7) * 2;
-        s_addr[j] = 0;
-      } else {
-        const int col = bcol[j] + lrow;
-        b_addr[j] = smem_addr + A_BYTES + col * 16 + 4 * lq;
-        s_addr[j] = smem_addr + A_BYTES + MXC_BYTES + col * 4;
-      }
+      const int col = bcol[j] + lrow;
+      b_addr[j] = smem_addr + A_BYTES + col * 16 + 4 * lq;
+      s_addr[j] = smem_addr + A_BYTES + MXC_BYTES + col * 4;
     }
   }
 
@@ -304,8 +260,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   // MFMA reads it.
   bf16x8_t xa0, xa1, xa2, xa3, xb0, xb1;
   bf16x8_t ya0, ya1, ya2, ya3, yb0, yb1;
-  s16x4_t h0, h1, h2, h3;          // bf16: transposed fragment halves
-  uint32_t cw0, cw1, sw0, sw1;     // MXFP4: code words and scales of B 0, 1
+  uint32_t cw0, cw1, sw0, sw1;  // code words and scales of B 0, 1
 #define G_MF                                                                         \
   "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"                        \
   "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"                        \
@@ -328,11 +283,6 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   "ds_read_b128 %[na1], %[aa] offset:2048\n\t"                                       \
   "ds_read_b128 %[na2], %[aa] offset:4096\n\t"                                       \
   "ds_read_b128 %[na3], %[aa] offset:6144\n\t"
-#define G_RB_BF16(OFF0, OFF1)                                                        \
-  "ds_read_b64_tr_b16 %[h0], %[ba0] offset:" OFF0 "\n\t"                             \
-  "ds_read_b64_tr_b16 %[h1], %[ba0] offset:" OFF1 "\n\t"                             \
-  "ds_read_b64_tr_b16 %[h2], %[ba1] offset:" OFF0 "\n\t"                             \
-  "ds_read_b64_tr_b16 %[h3], %[ba1] offset:" OFF1 "\n\t"
 #define G_RB_MX(OFF)                                                                 \
   "ds_read_b32 %[cw0], %[ba0] offset:" OFF "\n\t"                                    \
   "ds_read_b32 %[cw1], %[ba1] offset:" OFF "\n\t"                                    \
@@ -342,28 +292,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
   [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]),               \
       [c11] "+v"(acc[1][1]), [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]),           \
       [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1])
-  // reads of a half-step into set N (A at AA; bf16 B at BA0/BA1 + OFF0/OFF1;
-  // MXFP4 codes at BA0/BA1 + MXOFF, scales at SA0/SA1) while the MFMAs
-  // (string MF) consume set C; then set N's B fragments are assembled or
-  // converted
-#define G_BLOCK(OFF0, OFF1, MXOFF, AA, BA0, BA1, SA0, SA1, N, C, MF, ...)            \
+  // reads of a half-step into set N (A at AA; codes at BA0/BA1 + MXOFF,
+  // scales at SA0/SA1) while the MFMAs (string MF) consume set C; then set
+  // N's B fragments are converted
+#define G_BLOCK(MXOFF, AA, BA0, BA1, SA0, SA1, N, C, MF, ...)                         \
   do {                                                                               \
-    if (!MX) {                                                                       \
-      asm volatile("s_nop 4\n\t" G_RA                                                \
-                   G_RB_BF16(OFF0, OFF1)                                             \
-                   MF "s_waitcnt lgkmcnt(0)"                                         \
-                   : [na0] "=&v"(N##a0), [na1] "=&v"(N##a1), [na2] "=&v"(N##a2),      \
-                     [na3] "=&v"(N##a3), [h0] "=&v"(h0), [h1] "=&v"(h1),              \
-                     [h2] "=&v"(h2), [h3] "=&v"(h3), G_ACC                           \
-                   : [a0] "v"(C##a0), [a1] "v"(C##a1), [a2] "v"(C##a2),               \
-                     [a3] "v"(C##a3), [b0] "v"(C##b0), [b1] "v"(C##b1),               \
-                     [aa] "v"(AA), [ba0] "v"(BA0), [ba1] "v"(BA1), __VA_ARGS__        \
-                   : "memory", "m0");                                                \
-      const s16x8_t v0 = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};   \
-      const s16x8_t v1 = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};   \
-      N##b0 = __builtin_bit_cast(bf16x8_t, v0);                                      \
-      N##b1 = __builtin_bit_cast(bf16x8_t, v1);                                      \
-    } else {                                                                         \
       asm volatile("s_nop 4\n\t" G_RA G_RB_MX(MXOFF) MF                               \
                    "s_waitcnt lgkmcnt(0)"                                            \
                    : [na0] "=&v"(N##a0), [na1] "=&v"(N##a1), [na2] "=&v"(N##a2),      \
@@ -375,7 +308,6 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
                      [sa1] "v"(SA1), __VA_ARGS__                                     \
                    : "memory", "m0");                                                \
       mx_fragments(cw0, sw0, cw1, sw1, N##b0, N##b1);                                \
-    }                                                                                \
   } while (0)
   // MFMAs only, on set y (the last half-step)
 #define G_MMA(MF)                                                                    \
@@ -417,17 +349,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     }
   } else {
     // fragments of half-step (0, 0) -> set x
-    if (!MX) {
-      asm volatile(G_RA G_RB_BF16("0", "2048") "s_waitcnt lgkmcnt(0)"
-                   : [na0] "=&v"(xa0), [na1] "=&v"(xa1), [na2] "=&v"(xa2), [na3] "=&v"(xa3),
-                     [h0] "=&v"(h0), [h1] "=&v"(h1), [h2] "=&v"(h2), [h3] "=&v"(h3)
-                   : [aa] "v"(a_addr[0]), [ba0] "v"(b_addr[0]), [ba1] "v"(b_addr[1])
-                   : "memory");
-      const s16x8_t v0 = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-      const s16x8_t v1 = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
-      xb0 = __builtin_bit_cast(bf16x8_t, v0);
-      xb1 = __builtin_bit_cast(bf16x8_t, v1);
-    } else {
+    {
       asm volatile(G_RA G_RB_MX("0") "s_waitcnt lgkmcnt(0)"
                    : [na0] "=&v"(xa0), [na1] "=&v"(xa1), [na2] "=&v"(xa2), [na3] "=&v"(xa3),
                      [cw0] "=&v"(cw0), [cw1] "=&v"(cw1), [sw0] "=&v"(sw0), [sw1] "=&v"(sw1)
@@ -447,58 +369,36 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     uint32_t si = (uint32_t)(NST - 1) * SB;  // stage of step kt - 1 + NST
     auto next_stage = [](uint32_t o) { return o + SB == NST * SB ? 0u : o + SB; };
     {
-      // Pairs of steps (kt even, kt + 1 odd) that both issue copies, with
-      // the copies inside the asm blocks. Copy destinations (M0): A copy r
-      // of wave w at stage + 8192 r + 1024 w, bf16 B copy r at stage +
-      // A_BYTES + 2048 w + 1024 r. (MXFP4 B copies, one per thread and step,
-      // of a size that depends on the wave, stay between the blocks.)
+      // Pairs of steps (kt even, kt + 1 odd) that both issue copies, the A
+      // copies inside the asm blocks (M0: A copy r of wave w at stage +
+      // 8192 r + 1024 w). The B copies, one per thread and step, of a size
+      // that depends on the wave, stay between the blocks.
       const uint32_t lds_a = __builtin_amdgcn_readfirstlane(smem_addr + wave * 1024);
-      const uint32_t lds_b = __builtin_amdgcn_readfirstlane(smem_addr + A_BYTES + wave * 2048);
       for (; kt + NST < nk; kt += 2) {
         const uint32_t so1 = next_stage(so), so2 = next_stage(so1), si1 = next_stage(si);
         // step kt: copies of step kt - 1 + NST into the stage of step kt - 1
         int is = kt - 1 + NST;
         uint64_t ga0 = (uint64_t)(a_g[0] + is * BK), ga1 = (uint64_t)(a_g[1] + is * BK);
-        G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
-                s_addr[0] + so, s_addr[1] + so, y, x, G_MF_CP(G_CP16(0), "", G_CP16(1), ""),
-                [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si), [m1] "s"(lds_a + si + 8192));
-        if (!MX) {
-          const uint64_t gb0 = (uint64_t)(b_g[0] + (size_t)is * BK * N * 2);
-          const uint64_t gb1 = (uint64_t)(b_g[1] + (size_t)is * BK * N * 2);
-          G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
-                  s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF_CP(G_CP16(0), "", G_CP16(1), ""),
-                  [g0] "v"(gb0), [g1] "v"(gb1), [m0] "s"(lds_b + si), [m1] "s"(lds_b + si + 1024));
-        } else {
-          G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
-                  s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF, G_NOCOPY);
-          issue_b(is, si);
-        }
+        G_BLOCK("8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, s_addr[0] + so,
+                s_addr[1] + so, y, x, G_MF_CP(G_CP16(0), "", G_CP16(1), ""), [g0] "v"(ga0),
+                [g1] "v"(ga1), [m0] "s"(lds_a + si), [m1] "s"(lds_a + si + 8192));
+        G_BLOCK("0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1, s_addr[0] + so1,
+                s_addr[1] + so1, x, y, G_MF, G_NOCOPY);
+        issue_b(is, si);
         // step kt + 1: after the barrier, copies of step kt + NST into the
         // stage of step kt
-        G_BLOCK("8192", "10240", "8", a_addr[1] + so1, b_addr[0] + so1, b_addr[1] + so1,
-                s_addr[0] + so1, s_addr[1] + so1, y, x, G_MF, G_NOCOPY);
+        G_BLOCK("8", a_addr[1] + so1, b_addr[0] + so1, b_addr[1] + so1, s_addr[0] + so1,
+                s_addr[1] + so1, y, x, G_MF, G_NOCOPY);
         wait_vmcnt<PER * (NST - 4)>();  // steps up to kt + 3 have landed
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         is = kt + NST;
         ga0 = (uint64_t)(a_g[0] + is * BK);
         ga1 = (uint64_t)(a_g[1] + is * BK);
-        if (!MX) {
-          const uint64_t gb0 = (uint64_t)(b_g[0] + (size_t)is * BK * N * 2);
-          const uint64_t gb1 = (uint64_t)(b_g[1] + (size_t)is * BK * N * 2);
-          G_BLOCK("0", "2048", "0", a_addr[0] + so2, b_addr[0] + so2, b_addr[1] + so2,
-                  s_addr[0] + so2, s_addr[1] + so2, x, y,
-                  G_MF_CP(G_CP16(0), G_CP16(1), G_CP16(2), G_CP16(3)),
-                  [g0] "v"(ga0), [g1] "v"(ga1), [g2] "v"(gb0), [g3] "v"(gb1),
-                  [m0] "s"(lds_a + si1), [m1] "s"(lds_a + si1 + 8192), [m2] "s"(lds_b + si1),
-                  [m3] "s"(lds_b + si1 + 1024));
-        } else {
-          G_BLOCK("0", "2048", "0", a_addr[0] + so2, b_addr[0] + so2, b_addr[1] + so2,
-                  s_addr[0] + so2, s_addr[1] + so2, x, y, G_MF_CP(G_CP16(0), "", G_CP16(1), ""),
-                  [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si1),
-                  [m1] "s"(lds_a + si1 + 8192));
-          issue_b(is, si1);
-        }
+        G_BLOCK("0", a_addr[0] + so2, b_addr[0] + so2, b_addr[1] + so2, s_addr[0] + so2,
+                s_addr[1] + so2, x, y, G_MF_CP(G_CP16(0), "", G_CP16(1), ""), [g0] "v"(ga0),
+                [g1] "v"(ga1), [m0] "s"(lds_a + si1), [m1] "s"(lds_a + si1 + 8192));
+        issue_b(is, si1);
         so = so2;
         si = next_stage(si1);
       }
@@ -507,8 +407,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
     for (; kt + 1 < nk; ++kt) {
       const uint32_t so1 = so + SB == NST * SB ? 0u : so + SB;
       const int is = kt - 1 + NST;  // step whose copies this iteration issues
-      G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
-              s_addr[0] + so, s_addr[1] + so, y, x, G_MF, G_NOCOPY);
+      G_BLOCK("8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, s_addr[0] + so,
+              s_addr[1] + so, y, x, G_MF, G_NOCOPY);
       if (kt & 1) {
         // certify steps kt+1 and kt+2; every wave is done with steps < kt+1
         wait_copy_groups<PER>(min(nk - 1, kt - 2 + NST) - min(kt + 2, nk - 1));
@@ -516,16 +416,16 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
         asm volatile("" ::: "memory");
       }
       if (is < nk) issue_a(is, si);
-      G_BLOCK("0", "2048", "0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1,
-              s_addr[0] + so1, s_addr[1] + so1, x, y, G_MF, G_NOCOPY);
+      G_BLOCK("0", a_addr[0] + so1, b_addr[0] + so1, b_addr[1] + so1, s_addr[0] + so1,
+              s_addr[1] + so1, x, y, G_MF, G_NOCOPY);
       if (is < nk) issue_b(is, si);
       so = so1;
       si = next_stage(si);
     }
     // last step; these blocks end with the MFMA result wait states since
     // the compiler may move accumulators right after them
-    G_BLOCK("8192", "10240", "8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so,
-            s_addr[0] + so, s_addr[1] + so, y, x, G_MF MFMA_TAIL, G_NOCOPY);
+    G_BLOCK("8", a_addr[1] + so, b_addr[0] + so, b_addr[1] + so, s_addr[0] + so,
+            s_addr[1] + so, y, x, G_MF MFMA_TAIL, G_NOCOPY);
     G_MMA(G_MF MFMA_TAIL);
   }
   // the last MFMAs finish writing the accumulators before any VALU reads them
@@ -534,7 +434,6 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
 #undef G_BLOCK
 #undef G_ACC
 #undef G_RB_MX
-#undef G_RB_BF16
 #undef G_RA
 #undef G_MF
 
@@ -581,6 +480,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(Args a) {
 
 hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
+  if (!p.mxfp4) return launch_gemm16(p, mode == MODE_SWIGLU, s);
   Args a;
   a.A = p.A;
   a.gather = p.gather;
@@ -603,13 +503,8 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, hipStream_t s) {
   // an XCD's share of the worst-case tiles plus the split parts of its last round
   const long long total = (long long)a.max_tiles * a.n_tiles_n;
   const dim3 grid(8 * (ceil_div(total, 8) + kCUsPerXCD));
-  if (mode == MODE_SWIGLU) {
-    if (p.mxfp4) gemm_kernel<MODE_SWIGLU, true><<<grid, 512, 0, s>>>(a);
-    else gemm_kernel<MODE_SWIGLU, false><<<grid, 512, 0, s>>>(a);
-  } else {
-    if (p.mxfp4) gemm_kernel<MODE_DOWN, true><<<grid, 512, 0, s>>>(a);
-    else gemm_kernel<MODE_DOWN, false><<<grid, 512, 0, s>>>(a);
-  }
+  if (mode == MODE_SWIGLU) gemm_kernel<MODE_SWIGLU><<<grid, 512, 0, s>>>(a);
+  else gemm_kernel<MODE_DOWN><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -161,26 +161,22 @@ __device__ __forceinline__ bool schedule_tile(const Args& a, int b, Job& j) {
   return true;
 }
 
-// Split tiles: partial sums through the workspace. A slot holds the
-// 256 x 256 accumulators in register order, 16 bytes per lane per store:
-// float4 (wave, q, lane) with q = 4 (2i + j) + r/4 holds acc[i][j][r..r+3].
-// Parts 0..S-2 store theirs, raise their flag and return false; part S-1
-// adds the others' in part order and returns true (it runs the epilogue).
-__device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, f32x16_t (&acc)[4][2],
+// Split tiles: partial sums through the workspace. A slot holds a tile's
+// 256 x 256 accumulators in register order: each lane's 128 accumulators as
+// 32 float4, slot entry (wave, q, lane) holding float4 q of the lane (16
+// bytes per lane per store). get(q) returns the lane's float4 q, add(q, v)
+// adds v to it. Parts 0..S-2 store theirs, raise their flag and return
+// false; part S-1 adds the others' in part order and returns true (it runs
+// the epilogue).
+template <class Get, class Add>
+__device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, Get get, Add add,
                                                int wave, int lane, int tid) {
   const int S = jb.S, part = jb.part, slot0 = jb.slot0;
   float4* mine = reinterpret_cast<float4*>(a.split_ws) + wave * 32 * 64 + lane;
   if (part < S - 1) {
     float4* dst = mine + (size_t)(slot0 + part) * (TM * TN / 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          dst[((2 * i + j) * 4 + rq) * 64] =
-              make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
-                          acc[i][j][4 * rq + 3]);
+    for (int q = 0; q < 32; ++q) dst[q * 64] = get(q);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();  // every wave's partial sums are in memory
     if (tid == 0) {
@@ -205,19 +201,31 @@ __device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, f32
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const float4* src = mine + (size_t)(slot0 + p) * (TM * TN / 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const float4 v = src[((2 * i + j) * 4 + rq) * 64];
-          acc[i][j][4 * rq] += v.x;
-          acc[i][j][4 * rq + 1] += v.y;
-          acc[i][j][4 * rq + 2] += v.z;
-          acc[i][j][4 * rq + 3] += v.w;
-        }
+    for (int q = 0; q < 32; ++q) add(q, src[q * 64]);
   }
   return true;
+}
+
+// split_exchange for the 32x32 accumulator layout acc[4][2] (f32x16):
+// float4 q = 4 (2i + j) + r/4 holds acc[i][j][r..r+3]
+__device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, f32x16_t (&acc)[4][2],
+                                               int wave, int lane, int tid) {
+  return split_exchange(
+      a, jb,
+      [&](int q) {
+        const f32x16_t& t = acc[q >> 3][(q >> 2) & 1];
+        const int r = 4 * (q & 3);
+        return make_float4(t[r], t[r + 1], t[r + 2], t[r + 3]);
+      },
+      [&](int q, float4 v) {
+        f32x16_t& t = acc[q >> 3][(q >> 2) & 1];
+        const int r = 4 * (q & 3);
+        t[r] += v.x;
+        t[r + 1] += v.y;
+        t[r + 2] += v.z;
+        t[r + 3] += v.w;
+      },
+      wave, lane, tid);
 }
 
 // Down-projection epilogue: the wave's 128 rows x 64 fp32 columns (rows
