@@ -91,7 +91,7 @@ def roofline_kernel(cfg):
         return {"name": "gemm_a8_kernel<0>", "src": "gemm_a8.hip", "bound": "mfma",
                 "peak": PEAK_FP8_TFLOPS}
     if cfg.wdt == 2:
-        return {"name": "gemm_kernel<0>", "src": "gemm.hip", "bound": "mfma"}
+        return {"name": "gemm16_mx_kernel<0>", "src": "gemm16.hip", "bound": "mfma"}
     return {"name": "gemm16_kernel<0>", "src": "gemm16.hip", "bound": "mfma"}
 
 

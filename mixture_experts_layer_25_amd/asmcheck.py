@@ -95,7 +95,7 @@ def compile_to_asm(src: str) -> str:
         return open(out).read()
 
 
-SOURCES = ("gemm.hip", "gemm16.hip", "gemm_a8.hip")
+SOURCES = ("gemm16.hip", "gemm_a8.hip")
 
 
 def main(argv=None) -> int:

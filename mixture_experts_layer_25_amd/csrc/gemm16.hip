@@ -1,29 +1,70 @@
-// Grouped expert GEMMs with bf16 activations and bf16 weights on the
-// 16x16x32 MFMA (v_mfma_f32_16x16x32_bf16).
+// Grouped expert GEMMs with bf16 activations on the 16x16x32 MFMA
+// (v_mfma_f32_16x16x32_bf16), bf16 weights (gemm16_kernel) or MXFP4 weights
+// converted to bf16 in registers (gemm16_mx_kernel), fp32 accumulate. MXFP8
+// activations with MXFP4 weights run on the block-scaled MFMA in gemm_a8.hip.
 //
 // "ops-transformer MoE operator on Ascend NPU", optimisation 3: every
-// expert's matmul in one launch. "FFN, SwiGLU and MoE" sec. 2:
-// H = SiLU(X W_gate) * (X W_up), Y = H W_down. "DeepSeek-V4.1-Flash
-// fine-grained MoE (5A)" sec. 1, 3: gate and up clamped before SiLU*up.
+// expert's matmul in one launch, with a different row count per expert.
+// "FFN, SwiGLU and MoE" sec. 2: H = SiLU(X W_gate) * (X W_up), Y = H W_down.
+// "DeepSeek-V4.1-Flash fine-grained MoE (5A)" sec. 1, 3: gate and up are
+// clamped to [-L, L] before SiLU(gate)*up; routed experts may be FP4 (here
+// MXFP4: e2m1 codes with an e8m0 scale per 32 K-elements).
 //
-// Tile, schedule, pipeline and epilogue as gemm_kernel (gemm.hip, MXFP4
-// weights): 256 rows x 256 B-columns per workgroup (SwiGLU: 128 gate and
-// the same 128 up columns), 8 waves of 128 rows x 64 B-columns, a ring of 5
-// stages of 32 KB filled by global_load_lds, one barrier per two steps, the
-// copies placed between the MFMAs. The MFMA shape differs: under full load
-// the GEMMs are power-bound, and the 16x16x32 instruction does the same
-// multiply-adds for less power than 32x32x16: back-to-back on every SIMD with
-// no memory traffic, 16x16x32 sustains 2.12-2.27 PFLOP/s where 32x32x16
-// sustains 1.80-2.06 (the clock settles higher).
+// Tile: 256 rows x 256 B-columns, 32 k per step, 512 threads (8 waves, two
+// per SIMD). SwiGLU: the 256 B-columns are 128 gate and the same 128 up
+// columns, so gate and up of the same (row, f) meet in one lane and the
+// epilogue forms h = SiLU(clamp(g)) * clamp(u) in registers and stores bf16
+// H; the gate/up intermediate never reaches memory. Down: 256 output
+// columns, fp32 stores. A square tile moves the fewest bytes per flop that
+// 64K fp32 accumulators per CU allow. Wave (wm, wn) owns rows 128wm.. and
+// 64 B-columns (SwiGLU: f = 32wn..32wn+31, gate and up).
 //
-// Operands in LDS. A (X rows, K-contiguous): 16-byte k-groups in rows of 64
-// bytes, slot = k-group ^ swz4(row), read with ds_read_b128. B ([K][N],
-// N-contiguous): k-rows of 512 bytes (32 chunks of 8 columns, slot = chunk ^
-// 4 (k mod 4)) stored as they are; the MFMA fragment (8 k of one column) is
-// read with the gfx950 transposing load ds_read_b64_tr_b16 (within a 16-lane
-// group, lane i receives element i of the 4 rows the group points at), two
-// per fragment, so no transpose runs on the vector ALUs. Both swizzles put
-// the 16 lanes of an LDS cycle in distinct bank groups.
+// Why 16x16x32: under full load these GEMMs are power-bound, and this MFMA
+// does the same multiply-adds for less power than 32x32x16. Back-to-back on
+// every SIMD with no memory traffic, 16x16x32 sustains 2.12-2.27 PFLOP/s
+// where 32x32x16 sustains 1.80-2.06 (the clock settles higher); the same
+// pipeline with 32x32x16 ran these GEMMs 6-9 % slower.
+//
+// Operands reach MFMA K-contiguous: a lane's fragment is 8 consecutive k of
+// one row (A) or one column (B).
+//   A (X rows, K-contiguous): copied as 16-byte pieces to LDS rows of 64
+//   bytes (4 k-groups, slot = k-group ^ swz4(row)), read with ds_read_b128.
+//   With a gather list (the fused layer passes perm_token), routed row r
+//   is copied from row gather[r] of x: each copy lane looks its two row
+//   addresses up once per tile, so the dispatched copy of x is never built.
+//   B bf16 ([K][N], N-contiguous): k-rows of 512 bytes (32 chunks of 8
+//   columns, slot = chunk ^ 4 (k mod 4)) stored as they are; the fragment
+//   is read with the gfx950 transposing load ds_read_b64_tr_b16 (within a
+//   16-lane group, lane i receives element i of the 4 rows the group points
+//   at), two per fragment, so no transpose runs on the vector ALUs.
+//   B MXFP4 (stored by 32-k blocks, block-major, so that a step's codes of
+//   consecutive columns are consecutive 16-byte pieces): each column's 16
+//   code bytes of the step and its e8m0 scale are copied to LDS; a lane
+//   reads the 4 code bytes of its k-group and the scale and converts them
+//   exactly to bf16 (mxfp4.h). The weights cross HBM, L2 and LDS at 4 bits.
+// The swizzles put the 16 lanes of each 256-byte LDS cycle (64 banks on
+// gfx950) in distinct bank groups.
+//
+// Pipeline. Global data goes straight to LDS with global_load_lds (no
+// register staging) into a ring of stages (5 x 32 KB for bf16 weights,
+// 7 x 21 KB for MXFP4). One barrier per two steps, in the middle of every
+// odd step kt, certifies the copies of steps kt+1 and kt+2 and that every
+// wave is done reading the stages of steps up to kt; each step issues the
+// copies of step kt - 1 + NSTAGE (into the stage of step kt - 1). The copy
+// instructions sit between the MFMAs of the asm blocks (an even step puts
+// its copies into both of its blocks, an odd step all of them after its
+// barrier, where the stage of step kt - 1 becomes free), so that a copy
+// whose issue waits for room in the memory pipeline stalls while the MFMA
+// pipe is busy anyway; issued between the blocks, the copies cost a fifth
+// more cycles per step. (MXFP4 B copies, whose size depends on the wave,
+// stay between the blocks.)
+//
+// Tile schedule (schedule_tile, gemm_tile.h): the real tiles, in
+// expert_tile_of order, are cut into 8 contiguous ranges, one per XCD
+// (workgroup b runs on XCD b mod 8). Whole rounds of 32 tiles (one per CU
+// of the XCD) run as whole tiles; the tiles of the last, partial round are
+// split along K so that the last round keeps every CU busy, their fp32
+// partial sums meeting in a workspace in a fixed order.
 //
 // MFMA lane layout (checked on the device against a CPU product): lane l
 // supplies row l%16 of A and column l%16 of B, each with k = 8 (l/16) ..
@@ -45,6 +86,7 @@
 // fragment 3 is needed last in the first half: its read has 12 MFMAs to
 // land, and the block waits for it (lgkmcnt) only before those MFMAs.
 #include "gemm_tile.h"
+#include "mxfp4.h"
 
 namespace moe {
 namespace {
@@ -58,6 +100,96 @@ constexpr int PER16 = 4;                   // copies per thread per step
 
 typedef short s16x4_16 __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Split-tile exchange and epilogue of a 16x16-layout tile (accumulator r of
+// lane l in tile (i, j): row 16i + 4 (l/16) + r, column bcol[j] + l%16).
+// SwiGLU: bf16 h = SiLU(clamp(g)) * clamp(u), gate in column tiles 0, 1 and
+// the matching up in 2, 3; down: fp32 y. Both leave through LDS as 16-byte
+// stores.
+template <int MODE>
+__device__ __forceinline__ void finish_tile16(const Args& a, const Job& jb, f32x4_t (&acc)[8][4],
+                                              unsigned char* smem, int wave, int lane, int tid,
+                                              int n0) {
+  const int wm = wave >> 2, wn = wave & 3, l16 = lane & 15, g = lane >> 4;
+  const int row0 = jb.row0, row_end = jb.row_end, N = a.N;
+  // ---- split tiles: partial sums through the workspace (float4 q = 4 i + j)
+  if (jb.S > 1 && !split_exchange(
+                      a, jb,
+                      [&](int q) {
+                        const f32x4_t& t = acc[q >> 2][q & 3];
+                        return make_float4(t[0], t[1], t[2], t[3]);
+                      },
+                      [&](int q, float4 v) {
+                        f32x4_t& t = acc[q >> 2][q & 3];
+                        t[0] += v.x;
+                        t[1] += v.y;
+                        t[2] += v.z;
+                        t[3] += v.w;
+                      },
+                      wave, lane, tid))
+    return;
+
+  // ---- epilogue through LDS (16-byte global stores). Accumulator r of lane
+  // l in tile (i, j): row 16i + 4 (l/16) + r, column bcol[j] + l%16.
+  __syncthreads();  // every wave is done with the operand stages
+  if (MODE == MODE_SWIGLU) {
+    // wave tile: 128 rows x 32 f of bf16 h = SiLU(clamp(g)) * clamp(u),
+    // gate in column tiles 0, 1 and the matching up in 2, 3
+    unsigned char* wl = smem + wave * (128 * 64);
+    const bool clampit = a.clamp > 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * i + 4 * g + r;
+          float gv = acc[i][j][r], uv = acc[i][j + 2][r];
+          if (clampit) {
+            gv = __builtin_amdgcn_fmed3f(gv, -a.clamp, a.clamp);
+            uv = __builtin_amdgcn_fmed3f(uv, -a.clamp, a.clamp);
+          }
+          // SiLU(g) u with the hardware exp2 and reciprocal and the hardware
+          // round-to-nearest-even bf16 conversion
+          const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          *reinterpret_cast<__bf16*>(wl + m * 64 + (16 * j + l16) * 2) = (__bf16)h;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own wave's tile only
+    uint16_t* H = static_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane, m = idx >> 2, ch = idx & 3;
+      const int grow = row0 + 128 * wm + m, f = n0 + 32 * wn + 8 * ch;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 64 + ch * 16);
+      if (grow < row_end && f < N) *reinterpret_cast<u32x4_t*>(H + (size_t)grow * N + f) = v;
+    }
+  } else {
+    // wave tile: 128 rows x 64 fp32 columns, in two halves of 32 columns
+    unsigned char* wl = smem + wave * (128 * 128);
+    float* Y = static_cast<float*>(a.out);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = 16 * i + 4 * g + r;
+            *reinterpret_cast<float*>(wl + m * 128 + (16 * jj + l16) * 4) = acc[i][2 * hh + jj][r];
+          }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int idx = it * 64 + lane, m = idx >> 3, ch = idx & 7;
+        const int grow = row0 + 128 * wm + m, n = n0 + 64 * wn + 32 * hh + 4 * ch;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 128 + ch * 16);
+        if (grow < row_end && n < N) *reinterpret_cast<u32x4_t*>(Y + (size_t)grow * N + n) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half overwrites
+    }
+  }
+}
 
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
@@ -76,7 +208,9 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
   const int K = a.K, N = a.N;
   const int n0 = MODE == MODE_SWIGLU ? nt * 128 : nt * 256;
 
-  // weight column of tile column c (0..255), as in gemm_kernel
+  // Weight column of tile column c (0..255): SwiGLU gate columns n0.. then
+  // the same up columns; columns past N read column 0 (any valid data,
+  // never stored).
   auto b_column = [&](int c, bool& up) __attribute__((always_inline)) {
     int col;
     if (MODE == MODE_SWIGLU) {
@@ -89,9 +223,10 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
     return col < N ? col : 0;
   };
 
-  // ---- copies (as gemm_kernel with bf16 weights): A entry p = 4m + s
-  // holds k-group s ^ swz4(m) of row m; B k-row slot c holds 8-column
-  // chunk c ^ 4 (k mod 4)
+  // ---- copies: A entry p = 4m + s (16 bytes) holds k-group s ^ swz4(m) of
+  // row m, copy r of wave w fills entries 512r + 64w .. +63; B k-row slot c
+  // holds 8-column chunk c ^ 4 (k mod 4), copy r of wave w fills k-rows
+  // 4w + 2r and 4w + 2r + 1 (lanes 0-31 and 32-63)
   const uint16_t* a_g[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -328,7 +463,6 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
 #undef NOCOPY
 #undef CP
 #undef BPIN
-#undef ACC16
 #undef HALF_X
 #undef HALF
 #undef RDA
@@ -343,86 +477,269 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
 #undef RB0
 #undef M16
 
-  // ---- split tiles: partial sums through the workspace (float4 q = 4 i + j)
-  if (jb.S > 1 && !split_exchange(
-                      a, jb,
-                      [&](int q) {
-                        const f32x4_t& t = acc[q >> 2][q & 3];
-                        return make_float4(t[0], t[1], t[2], t[3]);
-                      },
-                      [&](int q, float4 v) {
-                        f32x4_t& t = acc[q >> 2][q & 3];
-                        t[0] += v.x;
-                        t[1] += v.y;
-                        t[2] += v.z;
-                        t[3] += v.w;
-                      },
-                      wave, lane, tid))
-    return;
+  finish_tile16<MODE>(a, jb, acc, smem, wave, lane, tid, n0);
+}
 
-  // ---- epilogue through LDS (16-byte global stores). Accumulator r of lane
-  // l in tile (i, j): row 16i + 4 (l/16) + r, column bcol[j] + l%16.
-  __syncthreads();  // every wave is done with the operand stages
-  if (MODE == MODE_SWIGLU) {
-    // wave tile: 128 rows x 32 f of bf16 h = SiLU(clamp(g)) * clamp(u),
-    // gate in column tiles 0, 1 and the matching up in 2, 3
-    unsigned char* wl = smem + wave * (128 * 64);
-    const bool clampit = a.clamp > 0.0f;
+// ---- MXFP4 weights. A and the pipeline as above; B stage per step: the 16
+// code bytes of each of the 256 tile columns (column c at 16c) and each
+// column's e8m0 scale in a dword (at 4c), copied by waves 0-3 (codes, 16
+// bytes per lane) and 4-7 (scales, one byte per lane, zero-extended). Lane l's fragment of column tile j is the code
+// dword 4 (l/16) of column bcol[j] + l%16 (8 k) and that column's scale,
+// converted exactly to bf16 in registers (mx_fragments). The second half of
+// step kt reads the codes and scales of step kt + 1 into 8 registers; they
+// are converted after its MFMAs, once the fragments of step kt are dead, so
+// one set of B registers serves.
+constexpr int MXC16 = TN * 16;                      // 4 KB of codes per step
+constexpr int SBX = A16_BYTES + MXC16 + TN * 4;     // + 1 KB of scale dwords
+constexpr int NSTX = 7;                             // 147 KB of LDS
+constexpr int PERX = 3;                             // copies per thread per step
+
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm16_mx_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NSTX * SBX];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 2;
+  const int wn = wave & 3;
+
+  Job jb;
+  if (!schedule_tile<BK16>(a, blockIdx.x, jb)) return;
+  const int e = jb.e, row0 = jb.row0, row_end = jb.row_end, nt = jb.nt;
+  const int kt_begin = jb.kt_begin, nk = jb.nk;
+  const int K = a.K, N = a.N;
+  const int n0 = MODE == MODE_SWIGLU ? nt * 128 : nt * 256;
+
+  const uint16_t* a_g[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+  for (int r = 0; r < 2; ++r) {
+    const int p = 512 * r + tid, m = p >> 2, q = (p & 3) ^ swz4(m);
+    int arow = min(row0 + m, row_end - 1);
+    if (a.gather) arow = min((unsigned)a.gather[arow], (unsigned)(a.gather_rows - 1));
+    a_g[r] = static_cast<const uint16_t*>(a.A) + (size_t)arow * K + kt_begin * BK16 + 8 * q;
+  }
+  // block-major weights: step kt's codes of column col at ((e K/32 + kt) N +
+  // col) 16, its scale at (e K/32 + kt) N + col; tile columns past N read
+  // column 0 (never stored)
+  const unsigned char* b_g;
+  {
+    const int c = 64 * (wave & 3) + lane;
+    const bool up = MODE == MODE_SWIGLU && c >= 128;
+    int col = MODE == MODE_SWIGLU ? n0 + (c & 127) : n0 + c;
+    col = col < N ? col : 0;
+    if (wave < 4)
+      b_g = static_cast<const uint8_t*>(up ? a.B1 : a.B0) + (((size_t)e * (K / 32) + kt_begin) * N + col) * 16;
+    else
+      b_g = (up ? a.S1 : a.S0) + ((size_t)e * (K / 32) + kt_begin) * N + col;
+  }
+  // kt counts from kt_begin
+  auto issue_a = [&](int kt, uint32_t so) __attribute__((always_inline)) {
+    unsigned char* st = smem + so;
+    dma16(a_g[0] + kt * BK16, st + wave * 1024);
+    dma16(a_g[1] + kt * BK16, st + 8192 + wave * 1024);
+  };
+  auto issue_b = [&](int kt, uint32_t so) __attribute__((always_inline)) {
+    unsigned char* Bs = smem + so + A16_BYTES;
+    if (wave < 4) dma16(b_g + (size_t)kt * N * 16, Bs + wave * 1024);
+    else dma1(b_g + (size_t)kt * N, Bs + MXC16 + (wave - 4) * 256);
+  };
+
+  f32x4_t acc[8][4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 16 * i + 4 * g + r;
-          float gv = acc[i][j][r], uv = acc[i][j + 2][r];
-          if (clampit) {
-            gv = __builtin_amdgcn_fmed3f(gv, -a.clamp, a.clamp);
-            uv = __builtin_amdgcn_fmed3f(uv, -a.clamp, a.clamp);
-          }
-          // SiLU(g) u with the hardware exp2 and reciprocal and the hardware
-          // round-to-nearest-even bf16 conversion
-          const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-          *reinterpret_cast<__bf16*>(wl + m * 64 + (16 * j + l16) * 2) = (__bf16)h;
-        }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own wave's tile only
-    uint16_t* H = static_cast<uint16_t*>(a.out);
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // column tiles as in the bf16 kernel; relative to tile 0 they start 16,
+  // 128, 144 (SwiGLU) or 16, 32, 48 (down) columns further
+  constexpr int D2 = MODE == MODE_SWIGLU ? 128 : 32, D3 = D2 + 16;
+  const int l16 = lane & 15, g = lane >> 4;
+  const uint32_t base = lds_addr(smem);
+  uint32_t a_addr, c_addr, s_addr;
+  {
+    const int m = 128 * wm + l16;
+    a_addr = base + m * 64 + ((g ^ swz4(m)) * 16);
+    const int col0 = (MODE == MODE_SWIGLU ? 32 * wn : 64 * wn) + l16;
+    c_addr = base + A16_BYTES + col0 * 16 + 4 * g;
+    s_addr = base + A16_BYTES + MXC16 + col0 * 4;
+  }
+
+  bf16x8_t p0, p1, p2, p3, q0, q1, q2, q3, b0, b1, b2, b3;
+  uint32_t cw0, cw1, cw2, cw3, sw0, sw1, sw2, sw3;
+#define XM(C, A, B) "v_mfma_f32_16x16x32_bf16 %[" C "], %[" A "], %[" B "], %[" C "]\n\t"
+#define XHALF(X0, X1, X2, X3, X4, X5, X6, X7, X8, X9, X10, X11, X12, X13, X14, X15)    \
+  XM("c00", "x0", "b0") X0 XM("c10", "x1", "b0") X1 XM("c20", "x2", "b0") X2           \
+  XM("c30", "x3", "b0") X3 XM("c01", "x0", "b1") X4 XM("c11", "x1", "b1") X5           \
+  XM("c21", "x2", "b1") X6 XM("c31", "x3", "b1") X7 XM("c02", "x0", "b2") X8           \
+  XM("c12", "x1", "b2") X9 XM("c22", "x2", "b2") X10 XM("c32", "x3", "b2") X11         \
+  XM("c03", "x0", "b3") X12 XM("c13", "x1", "b3") X13 XM("c23", "x2", "b3") X14        \
+  XM("c33", "x3", "b3") X15
+#define XHALF_X(...) XHALF(__VA_ARGS__)
+#define XRDA(OUT, OFF) "ds_read_b128 %[" OUT "], %[aa] offset:" OFF "\n\t"
+#define XRDC(OUT, OFF) "ds_read_b32 %[" OUT "], %[cb] offset:%[" OFF "]\n\t"
+#define XRDS(OUT, OFF) "ds_read_b32 %[" OUT "], %[sb] offset:%[" OFF "]\n\t"
+#define XBIN [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3)
+#define XOFFS                                                                        \
+  [co1] "n"(16 * 16), [co2] "n"(16 * D2), [co3] "n"(16 * D3), [so1] "n"(4 * 16),      \
+      [so2] "n"(4 * D2), [so3] "n"(4 * D3)
+#define XREADS_B                                                                     \
+  [cw0] "=&v"(cw0), [cw1] "=&v"(cw1), [cw2] "=&v"(cw2), [cw3] "=&v"(cw3),              \
+      [sw0] "=&v"(sw0), [sw1] "=&v"(sw1), [sw2] "=&v"(sw2), [sw3] "=&v"(sw3)
+#define XCP(X) "s_mov_b32 m0, %[m" #X "]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[g" #X "], off\n\t"
+#define XNOCOPY [g0] "n"(0)
+  // first half of a step: P x B, reading Q of the step; C0, C1: copies
+#define H1X(SO, C0, C1, ...)                                                          \
+  asm volatile("s_nop 4\n\t"                                                         \
+               XHALF_X(XRDA("nq0", "4096"), C0, XRDA("nq1", "5120"), "", XRDA("nq2", "6144"), C1, \
+                       XRDA("nq3", "7168"), "", "", "", "", "", "", "", "", "")       \
+               "s_waitcnt lgkmcnt(0)"                                                \
+               : [nq0] "=&v"(q0), [nq1] "=&v"(q1), [nq2] "=&v"(q2), [nq3] "=&v"(q3),  \
+                 ACC16(0)                                                            \
+               : [x0] "v"(p0), [x1] "v"(p1), [x2] "v"(p2), [x3] "v"(p3), XBIN,        \
+                 [aa] "v"(a_addr + (SO)), __VA_ARGS__                                \
+               : "memory", "m0")
+  // second half: Q x B, reading P and the B codes and scales of the next step
+  // (stage offset SO)
+#define H2X(SO, C0, C1, ...)                                                          \
+  asm volatile("s_nop 4\n\t"                                                         \
+               XHALF_X(XRDA("np0", "0"), "ds_read_b32 %[cw0], %[cb]\n\t", XRDA("np1", "1024"), \
+                       "ds_read_b32 %[sw0], %[sb]\n\t", XRDA("np2", "2048"), C0,      \
+                       XRDA("np3", "3072"), XRDC("cw1", "co1"), XRDS("sw1", "so1"), C1, \
+                       XRDC("cw2", "co2"), XRDS("sw2", "so2"), XRDC("cw3", "co3"),    \
+                       XRDS("sw3", "so3"), "", "")                                    \
+               "s_waitcnt lgkmcnt(0)"                                                \
+               : [np0] "=&v"(p0), [np1] "=&v"(p1), [np2] "=&v"(p2), [np3] "=&v"(p3),  \
+                 XREADS_B, ACC16(4)                                                  \
+               : [x0] "v"(q0), [x1] "v"(q1), [x2] "v"(q2), [x3] "v"(q3), XBIN,        \
+                 [aa] "v"(a_addr + (SO)), [cb] "v"(c_addr + (SO)), [sb] "v"(s_addr + (SO)), \
+                 XOFFS, __VA_ARGS__                                                  \
+               : "memory", "m0")
+#define H2X_LAST()                                                                   \
+  asm volatile("s_nop 4\n\t" XHALF("", "", "", "", "", "", "", "", "", "", "", "", "", "", "", "") \
+               MFMA_TAIL                                                             \
+               : ACC16(4)                                                            \
+               : [x0] "v"(q0), [x1] "v"(q1), [x2] "v"(q2), [x3] "v"(q3), XBIN)
+#define CONVERT()                                                                    \
+  do {                                                                               \
+    mx_fragments(cw0, sw0, cw1, sw1, b0, b1);                                        \
+    mx_fragments(cw2, sw2, cw3, sw3, b2, b3);                                        \
+  } while (0)
+
+  const bool idle = __builtin_amdgcn_readfirstlane(row_end - row0 <= 128 * wm) != 0;
+
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 64 + lane, m = idx >> 2, ch = idx & 3;
-      const int grow = row0 + 128 * wm + m, f = n0 + 32 * wn + 8 * ch;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 64 + ch * 16);
-      if (grow < row_end && f < N) *reinterpret_cast<u32x4_t*>(H + (size_t)grow * N + f) = v;
+  for (int s = 0; s < NSTX - 1; ++s)
+    if (s < nk) {
+      issue_a(s, s * SBX);
+      issue_b(s, s * SBX);
+    }
+  wait_copy_groups<PERX>(min(NSTX - 2, nk - 1) - min(1, nk - 1));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  if (idle) {
+    uint32_t si = (uint32_t)(NSTX - 1) * SBX;
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const int is = kt - 1 + NSTX;
+      if (kt & 1) {
+        wait_copy_groups<PERX>(min(nk - 1, kt - 2 + NSTX) - min(kt + 2, nk - 1));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      if (is < nk) {
+        issue_a(is, si);
+        issue_b(is, si);
+      }
+      si = si + SBX == NSTX * SBX ? 0u : si + SBX;
     }
   } else {
-    // wave tile: 128 rows x 64 fp32 columns, in two halves of 32 columns
-    unsigned char* wl = smem + wave * (128 * 128);
-    float* Y = static_cast<float*>(a.out);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = 16 * i + 4 * g + r;
-            *reinterpret_cast<float*>(wl + m * 128 + (16 * jj + l16) * 4) = acc[i][2 * hh + jj][r];
-          }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int idx = it * 64 + lane, m = idx >> 3, ch = idx & 7;
-        const int grow = row0 + 128 * wm + m, n = n0 + 64 * wn + 32 * hh + 4 * ch;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + m * 128 + ch * 16);
-        if (grow < row_end && n < N) *reinterpret_cast<u32x4_t*>(Y + (size_t)grow * N + n) = v;
+    // P and the B fragments of step 0
+    asm volatile(XRDA("np0", "0") XRDA("np1", "1024") XRDA("np2", "2048") XRDA("np3", "3072")
+                 "ds_read_b32 %[cw0], %[cb]\n\tds_read_b32 %[sw0], %[sb]\n\t"
+                 XRDC("cw1", "co1") XRDS("sw1", "so1") XRDC("cw2", "co2") XRDS("sw2", "so2")
+                 XRDC("cw3", "co3") XRDS("sw3", "so3") "s_waitcnt lgkmcnt(0)"
+                 : [np0] "=&v"(p0), [np1] "=&v"(p1), [np2] "=&v"(p2), [np3] "=&v"(p3), XREADS_B
+                 : [aa] "v"(a_addr), [cb] "v"(c_addr), [sb] "v"(s_addr), XOFFS
+                 : "memory");
+    CONVERT();
+
+    int kt = 0;
+    uint32_t so = 0;
+    uint32_t si = (uint32_t)(NSTX - 1) * SBX;
+    auto next_stage = [](uint32_t o) { return o + SBX == NSTX * SBX ? 0u : o + SBX; };
+    {
+      // pairs of steps that both issue copies; the A copies inside the
+      // blocks (M0: copy r of wave w at stage + 8192 r + 1024 w), the B
+      // copies (one per thread, wave-dependent size) between them
+      const uint32_t lds_a = __builtin_amdgcn_readfirstlane(base + wave * 1024);
+      for (; kt + NSTX < nk; kt += 2) {
+        const uint32_t so1 = next_stage(so), so2 = next_stage(so1), si1 = next_stage(si);
+        int is = kt - 1 + NSTX;
+        uint64_t ga0 = (uint64_t)(a_g[0] + is * BK16), ga1 = (uint64_t)(a_g[1] + is * BK16);
+        H1X(so, XCP(0), XCP(1), [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si),
+            [m1] "s"(lds_a + si + 8192));
+        H2X(so1, "", "", XNOCOPY);
+        issue_b(is, si);
+        CONVERT();
+        H1X(so1, "", "", XNOCOPY);
+        wait_vmcnt<PERX * (NSTX - 4)>();  // steps up to kt + 3 have landed
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        is = kt + NSTX;
+        ga0 = (uint64_t)(a_g[0] + is * BK16);
+        ga1 = (uint64_t)(a_g[1] + is * BK16);
+        H2X(so2, XCP(0), XCP(1), [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si1),
+            [m1] "s"(lds_a + si1 + 8192));
+        issue_b(is, si1);
+        CONVERT();
+        so = so2;
+        si = next_stage(si1);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half overwrites
     }
+    for (; kt + 1 < nk; ++kt) {
+      const uint32_t so1 = next_stage(so);
+      const int is = kt - 1 + NSTX;
+      H1X(so, "", "", XNOCOPY);
+      if (kt & 1) {
+        wait_copy_groups<PERX>(min(nk - 1, kt - 2 + NSTX) - min(kt + 2, nk - 1));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      if (is < nk) issue_a(is, si);
+      H2X(so1, "", "", XNOCOPY);
+      if (is < nk) issue_b(is, si);
+      CONVERT();
+      so = so1;
+      si = next_stage(si);
+    }
+    H1X(so, "", "", XNOCOPY);
+    H2X_LAST();
   }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#undef CONVERT
+#undef H2X_LAST
+#undef H2X
+#undef H1X
+#undef XNOCOPY
+#undef XCP
+#undef XREADS_B
+#undef XOFFS
+#undef XBIN
+#undef XRDS
+#undef XRDC
+#undef XRDA
+#undef XHALF_X
+#undef XHALF
+#undef XM
+#undef ACC16
+
+  finish_tile16<MODE>(a, jb, acc, smem, wave, lane, tid, n0);
 }
 
 }  // namespace
+
+namespace {
 
 hipError_t launch_gemm16(const GemmProblem& p, bool swiglu, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
@@ -445,9 +762,21 @@ hipError_t launch_gemm16(const GemmProblem& p, bool swiglu, hipStream_t s) {
   a.out = p.out;
   const long long total = (long long)a.max_tiles * a.n_tiles_n;
   const dim3 grid(8 * (ceil_div(total, 8) + kCUsPerXCD));
-  if (swiglu) gemm16_kernel<MODE_SWIGLU><<<grid, 512, 0, s>>>(a);
-  else gemm16_kernel<MODE_DOWN><<<grid, 512, 0, s>>>(a);
+  if (p.mxfp4) {
+    a.S0 = p.S0;
+    a.S1 = p.S1;
+    if (swiglu) gemm16_mx_kernel<MODE_SWIGLU><<<grid, 512, 0, s>>>(a);
+    else gemm16_mx_kernel<MODE_DOWN><<<grid, 512, 0, s>>>(a);
+  } else {
+    if (swiglu) gemm16_kernel<MODE_SWIGLU><<<grid, 512, 0, s>>>(a);
+    else gemm16_kernel<MODE_DOWN><<<grid, 512, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s) { return launch_gemm16(p, true, s); }
+hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s) { return launch_gemm16(p, false, s); }
 
 }  // namespace moe

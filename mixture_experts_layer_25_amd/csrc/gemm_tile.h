@@ -1,7 +1,8 @@
 // Tile schedule, operand-copy helpers and the split-tile exchange shared by
-// the grouped GEMM kernels (gemm.hip: bf16 activations; gemm_a8.hip: MXFP8
-// activations with MXFP4 weights). Both compute 256 x 256 tiles with 8
-// waves; they differ in the k covered per step and in the operand formats.
+// the grouped GEMM kernels (gemm16.hip: bf16 activations; gemm_a8.hip: MXFP8
+// activations with MXFP4 weights). All compute 256 x 256 tiles with 8
+// waves; they differ in the k covered per step, the MFMA shape and the
+// operand formats.
 #pragma once
 
 #include "common.h"
@@ -85,16 +86,17 @@ __device__ __forceinline__ void wait_copy_groups(int groups) {
 }
 
 // Tile order, by expert: an expert's tiles are contiguous, in groups of up
-// to 8 of its M-tiles; inside a group N-tile major and M-tile minor. The 32
-// workgroups an XCD runs at once then cover about 8 M-tiles x 4 N-tiles of
-// one expert, so each weight slab is fetched once and shared by all those
-// M-tiles, and each activation slab by 4 N-tiles. With a tile map, M-tile
+// to 16 of its M-tiles; inside a group N-tile major and M-tile minor. The 32
+// workgroups an XCD runs at once then cover all M-tiles of one expert (up
+// to 16) for a few N-tiles, so each weight slab is fetched once and shared
+// by all those M-tiles, and each activation slab by the N-tiles. (Groups of
+// 8 M-tiles were 1 % slower on the 8-expert layer, groups of 2 10 %.) With a tile map, M-tile
 // t / NT and the tile's own belong to the same expert (an expert's tiles
 // span whole rows of NT), which gives the expert's first M-tile and count
 // without a search.
 __device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int32_t* tilemap,
                                                const int32_t* offsets, int& mt, int& nt) {
-  constexpr int MG = 8;
+  constexpr int MG = 16;
   int first = 0, m = MT;
   if (tilemap) {
     const int g = t / NT;

@@ -76,9 +76,6 @@ struct GemmProblem {
 };
 hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);
-// bf16 weights on the 16x16x32 MFMA (gemm16.hip); the two above use it for
-// bf16 weights and gemm.hip's kernel for MXFP4 weights
-hipError_t launch_gemm16(const GemmProblem& p, bool swiglu, hipStream_t s);
 
 // MXFP4 weights with MXFP8 activations: rows of bf16 -> MXFP8 (codes
 // [rows][K], scales [rows][K/32]), and the grouped GEMM on the scaled MFMA
