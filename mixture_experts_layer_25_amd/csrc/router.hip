@@ -373,7 +373,7 @@ hipError_t launch_dv(const RouterArgs& a, bool xbf16, hipStream_t s) {
 
 // Exactly 8 experts and D <= 4096: the whole W_r ([D][8] fp32, 128 KB) is
 // copied into LDS once, by asynchronous global->LDS copies, and x streams
-// through a ring of 4 chunks of 8 KB (32 tokens x 128 d bf16, or 64 d
+// through a ring of 4 chunks of 4 KB (16 tokens x 128 d bf16, or 64 d
 // fp32), also copied asynchronously, so that no register staging or
 // transposition sits between the loads and the chains. One lane per chain
 // (token tt, expert te); each 16 d take two (bf16) or four (fp32) 16-byte x
@@ -383,8 +383,9 @@ hipError_t launch_dv(const RouterArgs& a, bool xbf16, hipStream_t s) {
 // read 8 distinct bank groups. The ring is paced by explicit counter waits
 // and barriers, and the LDS reads wait for themselves, so that copies of
 // later chunks stay in flight while a chunk is summed.
-constexpr int kE8Tokens = 32;        // tokens per workgroup (4 waves)
-constexpr int kE8ChunkBytes = 8192;  // one x chunk
+constexpr int kE8Tokens = 16;                     // tokens per workgroup (2 waves)
+constexpr int kE8Threads = 8 * kE8Tokens;         // one lane per (token, expert)
+constexpr int kE8ChunkBytes = 256 * kE8Tokens;    // one x chunk: 256 bytes per token
 constexpr int kE8Ring = 4;           // x chunks in the ring
 constexpr int kE8MaxD = 4096;        // W_r rows that fit beside the ring
 
@@ -404,7 +405,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <bool XBF16>
-__global__ __launch_bounds__(256) void router_e8_kernel(RouterArgs a) {
+__global__ __launch_bounds__(kE8Threads) void router_e8_kernel(RouterArgs a) {
   constexpr int SX = XBF16 ? 2 : 4;
   constexpr int DKX = kE8ChunkBytes / (kE8Tokens * SX);  // d per chunk: 128 or 64
   static_assert(kE8Ring == 4, "the chunk loop is unrolled for 4 ring slots");
@@ -424,13 +425,13 @@ __global__ __launch_bounds__(256) void router_e8_kernel(RouterArgs a) {
   const int D = a.D;
   const int nch = (D + DKX - 1) / DKX;
 
-  // W_r copy: 16-byte pieces p = 256 i + tid of the D * 32 bytes
+  // W_r copy: 16-byte pieces p = kE8Threads i + tid of the D * 32 bytes
   const int wpieces = D * 2;
-  const int wper = (wpieces + 255) / 256;  // the same for every thread
+  const int wper = (wpieces + kE8Threads - 1) / kE8Threads;  // the same for every thread
   for (int i = 0; i < wper; ++i) {
-    const int p = min(256 * i + tid, wpieces - 1);
+    const int p = min(kE8Threads * i + tid, wpieces - 1);
     lds_copy16(reinterpret_cast<const unsigned char*>(a.W_r) + 16 * (size_t)p,
-               wl + 16 * (256 * i + 64 * wave));
+               wl + 16 * (kE8Threads * i + 64 * wave));
   }
   // x chunk c -> its ring slot: LDS piece q = 64 (2 wave + r) + lane holds
   // token q / 16, group (q % 16) ^ (token % 8)
@@ -611,8 +612,8 @@ hipError_t launch_router(const moe_cfg& c, const void* x, const float* W_r, cons
   // waves per SIMD where the token count allows
   if (c.E == 8 && c.D <= kE8MaxD) {
     dim3 grid(ceil_div(c.T, kE8Tokens));
-    if (b) router_e8_kernel<true><<<grid, 256, 0, s>>>(a);
-    else router_e8_kernel<false><<<grid, 256, 0, s>>>(a);
+    if (b) router_e8_kernel<true><<<grid, kE8Threads, 0, s>>>(a);
+    else router_e8_kernel<false><<<grid, kE8Threads, 0, s>>>(a);
     return hipGetLastError();
   }
   if (c.E <= 8) return launch_dv<8, 512, 128>(a, b, s);
