@@ -114,3 +114,13 @@ def test_zero_tokens():
     y = moe.forward(cfg, x, W_r, None, w)
     torch.cuda.synchronize()
     assert y.shape[0] == 1
+
+
+@pytest.mark.parametrize("wdt", [syn.BF16, syn.MXFP4], ids=["bf16", "mxfp4"])
+@pytest.mark.parametrize("D,F", [(32, 32), (160, 224), (224, 96), (256, 192)])
+def test_gemm_step_counts(wdt, D, F):
+    """GEMM K from 32 (one 32-k step: the copy ring's prologue alone) to 256
+    (8 steps): the pipeline's paired-step loop runs 0, 1 or 2 times for the
+    5-stage bf16 ring and 0 or 1 times for the 7-stage MXFP4 ring; N = 96,
+    160, 192 and 224 leave partly filled 128- or 256-column tiles."""
+    _run(BASE.replace(name=f"steps_D{D}_F{F}", D=D, F=F, wdt=wdt, T=150, E=4, k=2))
