@@ -382,7 +382,9 @@ hipError_t launch_dv(const RouterArgs& a, bool xbf16, hipStream_t s) {
 // 16-byte groups at slot group ^ (token mod 8), so the 8 tokens of a wave
 // read 8 distinct bank groups. The ring is paced by explicit counter waits
 // and barriers, and the LDS reads wait for themselves, so that copies of
-// later chunks stay in flight while a chunk is summed.
+// later chunks stay in flight while a chunk is summed. With bf16 x the
+// reads of the next 16 d are issued before the FMAs of the current 16 d
+// (one wave per SIMD cannot hide the read latency otherwise).
 constexpr int kE8Tokens = 16;                     // tokens per workgroup (2 waves)
 constexpr int kE8Threads = 8 * kE8Tokens;         // one lane per (token, expert)
 constexpr int kE8ChunkBytes = 256 * kE8Tokens;    // one x chunk: 256 bytes per token
@@ -475,6 +477,73 @@ __global__ __launch_bounds__(kE8Threads) void router_e8_kernel(RouterArgs a) {
     const uint32_t xbase = e8_lds_addr(slot) + tt * 256;
     uint32_t wa = e8_lds_addr(wrow) + (uint32_t)c * DKX * 32;
     int dd = 0;
+    if (XBF16 && dk == DKX) {
+      // A whole bf16 chunk (8 blocks of 16 d), software-pipelined: each asm
+      // block issues the LDS reads of the next 16 d, then runs the unpacks
+      // and the 16 FMAs of the current 16 d (in the same order as below:
+      // d ascending, one fused multiply-add each), then waits for its
+      // reads. Two register sets alternate.
+      e8_f2 wA[8], wB[8];
+      e8_u4 uA0, uA1, uB0, uB1;
+      float tmp;
+      auto xa = [&](int blk, int h) { return xbase + (((2 * blk + h) ^ sw) * 16); };
+#define E8_RD8(N, ADDR)                                                              \
+  "ds_read2_b32 %[" N "0], %[" ADDR "] offset1:8\n\t"                                \
+  "ds_read2_b32 %[" N "1], %[" ADDR "] offset0:16 offset1:24\n\t"                    \
+  "ds_read2_b32 %[" N "2], %[" ADDR "] offset0:32 offset1:40\n\t"                    \
+  "ds_read2_b32 %[" N "3], %[" ADDR "] offset0:48 offset1:56\n\t"                    \
+  "ds_read2_b32 %[" N "4], %[" ADDR "] offset0:64 offset1:72\n\t"                    \
+  "ds_read2_b32 %[" N "5], %[" ADDR "] offset0:80 offset1:88\n\t"                    \
+  "ds_read2_b32 %[" N "6], %[" ADDR "] offset0:96 offset1:104\n\t"                   \
+  "ds_read2_b32 %[" N "7], %[" ADDR "] offset0:112 offset1:120\n\t"
+#define E8_FMA2(U, I)                                                                \
+  "v_lshlrev_b32 %[t], 16, %[" U "]\n\t"                                              \
+  "v_fmac_f32 %[acc], %[t], %[w" #I "x]\n\t"                                          \
+  "v_and_b32 %[t], 0xffff0000, %[" U "]\n\t"                                          \
+  "v_fmac_f32 %[acc], %[t], %[w" #I "y]\n\t"
+#define E8_FMAS                                                                      \
+  E8_FMA2("u0", 0) E8_FMA2("u1", 1) E8_FMA2("u2", 2) E8_FMA2("u3", 3) E8_FMA2("u4", 4)  \
+  E8_FMA2("u5", 5) E8_FMA2("u6", 6) E8_FMA2("u7", 7)
+#define E8_CUR(W, U0, U1)                                                            \
+  [u0] "v"(U0.x), [u1] "v"(U0.y), [u2] "v"(U0.z), [u3] "v"(U0.w), [u4] "v"(U1.x),      \
+      [u5] "v"(U1.y), [u6] "v"(U1.z), [u7] "v"(U1.w), [w0x] "v"(W[0].x),               \
+      [w0y] "v"(W[0].y), [w1x] "v"(W[1].x), [w1y] "v"(W[1].y), [w2x] "v"(W[2].x),      \
+      [w2y] "v"(W[2].y), [w3x] "v"(W[3].x), [w3y] "v"(W[3].y), [w4x] "v"(W[4].x),      \
+      [w4y] "v"(W[4].y), [w5x] "v"(W[5].x), [w5y] "v"(W[5].y), [w6x] "v"(W[6].x),      \
+      [w6y] "v"(W[6].y), [w7x] "v"(W[7].x), [w7y] "v"(W[7].y)
+#define E8_NEXT(W, U0, U1)                                                           \
+  [n0] "=&v"(W[0]), [n1] "=&v"(W[1]), [n2] "=&v"(W[2]), [n3] "=&v"(W[3]),              \
+      [n4] "=&v"(W[4]), [n5] "=&v"(W[5]), [n6] "=&v"(W[6]), [n7] "=&v"(W[7]),          \
+      [nu0] "=&v"(U0), [nu1] "=&v"(U1)
+      // reads of block BLK into (NW, NU0, NU1) while block BLK - 1 in (CW,
+      // CU0, CU1) is summed
+#define E8_STEP(BLK, NW, NU0, NU1, CW, CU0, CU1)                                     \
+  asm volatile(E8_RD8("n", "na") "ds_read_b128 %[nu0], %[nx0]\n\t"                   \
+               "ds_read_b128 %[nu1], %[nx1]\n\t" E8_FMAS "s_waitcnt lgkmcnt(0)"         \
+               : E8_NEXT(NW, NU0, NU1), [acc] "+v"(acc), [t] "=&v"(tmp)               \
+               : E8_CUR(CW, CU0, CU1), [na] "v"(wa + 512 * (BLK)),                    \
+                 [nx0] "v"(xa(BLK, 0)), [nx1] "v"(xa(BLK, 1)))
+      asm volatile(E8_RD8("n", "na") "ds_read_b128 %[nu0], %[nx0]\n\t"
+                   "ds_read_b128 %[nu1], %[nx1]\n\ts_waitcnt lgkmcnt(0)"
+                   : E8_NEXT(wA, uA0, uA1)
+                   : [na] "v"(wa), [nx0] "v"(xa(0, 0)), [nx1] "v"(xa(0, 1)));
+      E8_STEP(1, wB, uB0, uB1, wA, uA0, uA1);
+      E8_STEP(2, wA, uA0, uA1, wB, uB0, uB1);
+      E8_STEP(3, wB, uB0, uB1, wA, uA0, uA1);
+      E8_STEP(4, wA, uA0, uA1, wB, uB0, uB1);
+      E8_STEP(5, wB, uB0, uB1, wA, uA0, uA1);
+      E8_STEP(6, wA, uA0, uA1, wB, uB0, uB1);
+      E8_STEP(7, wB, uB0, uB1, wA, uA0, uA1);
+      asm volatile(E8_FMAS : [acc] "+v"(acc), [t] "=&v"(tmp) : E8_CUR(wB, uB0, uB1));
+#undef E8_STEP
+#undef E8_NEXT
+#undef E8_CUR
+#undef E8_FMAS
+#undef E8_FMA2
+#undef E8_RD8
+      static_assert(!XBF16 || DKX == 128, "the pipelined path covers 8 blocks of 16 d");
+      dd = dk;
+    }
     // 16 d per block: 8 W_r pairs and 16 x values in flight at once
     for (; dd + 16 <= dk; dd += 16, wa += 512) {
       const int g = dd / (16 / SX);
