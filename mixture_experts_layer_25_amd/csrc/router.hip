@@ -207,6 +207,15 @@ __global__ __launch_bounds__(NTH) void router_kernel(RouterArgs a) {
         }
       }
     }
+    if (E == EP && wvec) {
+      // the chunk's [DK][E] floats are wsm's own layout: 16-byte stores
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) {
+        const int f = 4 * (tid + NTH * i);
+        if (f < DK * EP) *reinterpret_cast<float4*>(&wsm[buf][0][0] + f) = rw[i];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NWV; ++i) {
       const int f = 4 * (tid + NTH * i);
