@@ -98,7 +98,6 @@ constexpr int SB16 = A16_BYTES + B16_BYTES;
 constexpr int NST16 = 5;                   // 160 KB of LDS
 constexpr int PER16 = 4;                   // copies per thread per step
 
-typedef short s16x4_16 __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Split-tile exchange and epilogue of a 16x16-layout tile (accumulator r of

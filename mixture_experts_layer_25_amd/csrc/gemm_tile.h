@@ -45,9 +45,7 @@ struct Args {
   int32_t* split_flags;  // one ready flag per partial slot, zero between launches
 };
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Slot permutation of the 4 k-groups of a 64-byte A row: rows r..r+15 then
