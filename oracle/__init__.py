@@ -9,11 +9,15 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   router_logits   pinned: closed forms (zero rows, one-hot rows), float64 bound
   select_topk     pinned: brute-force rank count, tie rule, zero rows
   gate_weights    pinned: worked sqrt-softplus example, softplus tails,
-                  softmax sums, renorm sums, the two top-k orderings
+                  softmax sums, renorm sums, the two top-k orderings;
+                  sigmoid weights on non-zero logits with a selection bias
+                  (renorm 0 and 1) against numpy's exp
   dispatch        pinned: invariants, capacity 1228, brute-force segments
   double_to_bf16  pinned: all 2^32 fp32 patterns against torch's conversion
-  expert / shared pinned: E=1,k=1 SwiGLU against a numpy matmul chain,
+  expert_rows     pinned: E=1,k=1 SwiGLU against a numpy matmul chain,
                   clamp closed form, dense-masked brute force
+  shared_rows     pinned: numpy matmul chain over the decoded bf16 weights
+                  with torch's bf16 rounding of H, shared_F != F, active clamp
   forward_tokens  pinned: dense all-experts masked brute force
   e4m3 / e4m3_encode / mxfp8_quantize
                   pinned: format values, exhaustive midpoints and ties,

@@ -476,3 +476,91 @@ def test_shared_expert_added_once():
     r_wo = oracle.forward(inp3)
     assert np.allclose(r_with["y_exact"] - r_wo["y_exact"], oracle.shared_rows(inp2, np.arange(cfg.T)),
                        rtol=1e-12, atol=1e-12)
+
+
+def _bf16_round_torch(h):
+    """float64 -> nearest bf16 (ties to even) -> float64, by torch's own
+    conversion (through float32; exact for h that are fp32-representable to
+    within far less than half a bf16 ulp)."""
+    import torch
+    return torch.from_numpy(np.asarray(h, np.float64)).to(torch.bfloat16).double().numpy()
+
+
+def _shared_chain_np(inp, clamp, round_h, width=None):
+    """The shared SwiGLU by numpy matmuls over the decoded bf16 weights:
+    clamp(x Ws_gate), clamp(x Ws_up), h = SiLU(g) u rounded to bf16, h Ws_down.
+    `width` truncates the expert to its first columns (a planted mistake)."""
+    xd = syn.bf16_bits_to_f32(inp.x).astype(np.float64)
+    Wg = syn.bf16_bits_to_f32(inp.Ws_gate).astype(np.float64)
+    Wu = syn.bf16_bits_to_f32(inp.Ws_up).astype(np.float64)
+    Wd = syn.bf16_bits_to_f32(inp.Ws_down).astype(np.float64)
+    if width is not None:
+        Wg, Wu, Wd = Wg[:, :width], Wu[:, :width], Wd[:width]
+    return _dense_swiglu_np(xd, Wg, Wu, Wd, clamp, round_h=round_h)
+
+
+def test_shared_expert_against_independent_chain():
+    """The always-on shared expert ("DeepSeek-V4.1-Flash fine-grained MoE
+    (5A)" sec. 1 and 3: one bf16 SwiGLU expert next to the routed ones, and
+    every expert clamped) against numpy matmuls of the decoded weights with
+    torch's bf16 rounding of H. The shared width (96) differs from the routed
+    width (32) and the clamp (0.5) cuts about half of the pre-activations,
+    so using F for shared_F, skipping the clamp or skipping the bf16 rounding
+    of H each moves the result far outside the comparison bound (checked
+    below against the same chain with each mistake planted)."""
+    cfg = syn.Config("t", T=16, D=64, E=4, k=2, F=32, act=syn.BF16, wdt=syn.BF16,
+                     gating=syn.GATE_SQRT_SOFTPLUS, renorm=0, clamp=0.5, shared_F=96,
+                     bias="normal", bias_sigma=0.1, w_sigma=0.1)
+    inp = _tiny_inputs(cfg)
+    got = oracle.shared_rows(inp, np.arange(cfg.T))
+    L = float(np.float32(cfg.clamp))
+    ref = _shared_chain_np(inp, L, _bf16_round_torch)
+    # the clamp is active on a good share of the pre-activations
+    xd = syn.bf16_bits_to_f32(inp.x).astype(np.float64)
+    g = xd @ syn.bf16_bits_to_f32(inp.Ws_gate).astype(np.float64)
+    assert 0.2 < np.mean(np.abs(g) > L) < 0.8
+    # only the summation order differs: far below one bf16 step of H
+    assert np.allclose(got, ref, rtol=1e-9, atol=1e-12)
+    scale = np.abs(ref).max()
+    for wrong in (_shared_chain_np(inp, L, _bf16_round_torch, width=cfg.F),   # F for shared_F
+                  _shared_chain_np(inp, 0.0, _bf16_round_torch),              # no clamp
+                  _shared_chain_np(inp, L, None)):                            # H kept in double
+        assert np.abs(wrong - got).max() > 1e-4 * scale
+    # and through the whole layer: y - (y without the shared expert) is the chain
+    r_with = oracle.forward(inp)
+    r_wo = oracle.forward(_tiny_inputs(cfg.replace(shared_F=0)))
+    assert np.allclose(r_with["y_exact"] - r_wo["y_exact"], ref, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_sigmoid_weights_on_nonzero_logits_with_bias(renorm):
+    """Sigmoid gating ("MoE routing: Top-K, Expert-Choice and Sigmoid
+    Gating"): the weight of a selected expert is 1/(1+e^-s) of its raw logit
+    s, the selection bias steering only which experts are selected, and the
+    k weights divided by their sum when renormalised. Checked against numpy's
+    exp on non-zero logits with a non-zero bias; the selection itself against
+    a brute-force rank count on the fp32 keys. Weights taken from the key
+    (logit + bias) instead of the raw logit fail the comparison (checked)."""
+    rng = np.random.default_rng(11)
+    T, E, k = 48, 12, 3
+    logits = (rng.standard_normal((T, E)) * 2.0).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.7).astype(np.float32)
+    cfg = _cfg(T=T, E=E, k=k, gating=syn.GATE_SIGMOID, renorm=renorm)
+    idx = oracle.select_topk(cfg, logits, bias)
+    keys = logits + bias   # one fp32 add per key
+    for t in range(T):
+        assert idx[t].tolist() == _brute_topk(keys[t].tolist(), k)
+    # the bias changes the selection on these inputs
+    assert not np.array_equal(idx, oracle.select_topk(cfg, logits, None))
+    w = oracle.gate_weights(cfg, logits, bias, idx).astype(np.float64)
+    s = np.take_along_axis(logits, idx, 1).astype(np.float64)
+    want = 1.0 / (1.0 + np.exp(-s))
+    if renorm:
+        want = want / want.sum(1, keepdims=True)
+        assert np.allclose(w.sum(1), 1.0, rtol=0, atol=k * 2.0**-23)
+    assert np.allclose(w, want, rtol=2.0**-23, atol=0)
+    kb = np.take_along_axis(keys, idx, 1).astype(np.float64)
+    wrong = 1.0 / (1.0 + np.exp(-kb))
+    if renorm:
+        wrong = wrong / wrong.sum(1, keepdims=True)
+    assert np.abs(wrong - w).max() > 1e-3
