@@ -4,7 +4,8 @@
  * C ABI. Every pointer argument is a DEVICE pointer unless marked (host).
  * The caller owns every buffer (inputs, outputs and the workspace); the
  * library never allocates or frees memory, never synchronises the stream and
- * keeps no state between calls. Every call validates its arguments on the
+ * keeps no state between calls (except the wait limit of
+ * moe_set_split_wait). Every call validates its arguments on the
  * host and then only enqueues kernels on `stream` (a hipStream_t passed as
  * void*; NULL means the default stream); results are ready once the stream
  * reaches that point. No C++ exception crosses this boundary.
@@ -134,9 +135,9 @@ typedef struct moe_weights {
 /* Bytes of workspace a call needs (host out-parameter `bytes`).
  * MOE_WS_DISPATCH for moe_dispatch (per-chunk expert counts),
  * MOE_WS_EXPERT_FFN for moe_expert_ffn / _gate_up / _down (the device tile
- * map and, with bf16 activations, 64 MiB of fp32 partial sums plus ready
- * flags for the GEMM tiles that are split along K), MOE_WS_FORWARD for
- * moe_forward (all of the above plus H, y_perm, x_perm for fp32
+ * map and, with bf16 activations, 64 MiB of fp32 partial sums plus two
+ * banks of ready flags for the GEMM tiles that are split along K),
+ * MOE_WS_FORWARD for moe_forward (all of the above plus H, y_perm, x_perm for fp32
  * activations only, the MXFP8 copy of x for MOE_MXFP4_A8 and, with a
  * shared expert, its H and output). A workspace carries state only within
  * one call; calls that run concurrently need separate workspaces. */
@@ -218,6 +219,21 @@ int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float
  * and rows >= 0; inputs are expected to be finite. */
 int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                        void* stream);
+
+/* Split-tile hand-off of the grouped GEMMs (bf16 activations). The tiles
+ * of a launch's last, partial round of workgroups are split along K: each
+ * earlier part leaves fp32 partial sums in the workspace and raises a ready
+ * flag, and the last part adds them in part order before the epilogue. The
+ * last part polls each flag at most `polls` times (default 2^24, about a
+ * second) and, if it does not rise, stores NaN (bf16 / fp32 NaN; in
+ * MXFP8 H the NaN codes and the e8m0 NaN scale 0xFF) for the outputs of
+ * that tile instead of a partial sum, so a failed hand-off cannot pass for
+ * a result; every workgroup still exits normally. polls = 0 makes every
+ * split tile give up at once (for testing that path). The setting is
+ * process-wide and the one piece of state the library keeps; it applies to
+ * launches enqueued after the call. Returns the previous value, or
+ * MOE_ERR_INVALID_ARG for polls < 0. */
+int moe_set_split_wait(int polls);
 
 /* Static text for a moe_status value (host pointer, never NULL). */
 const char* moe_status_string(int status);

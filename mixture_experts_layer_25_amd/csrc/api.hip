@@ -4,12 +4,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "launch.h"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+// polls of a split part's ready flag before its consumer gives up
+// (moe_set_split_wait)
+std::atomic<int> g_split_wait{moe::kSplitWaitDefault};
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
@@ -151,6 +156,7 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
   g.clamp = c.clamp;
   g.split_flags = split_flags_of(c, tilemap);
   g.split_ws = split_ws_of(c, tilemap);
+  g.split_wait = g_split_wait.load(std::memory_order_relaxed);
   return g;
 }
 
@@ -205,6 +211,7 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
     if (e != hipSuccess) return e;
   }
   moe::GemmProblem g = routed_problem(c, offsets, tilemap);
+  if (g.split_flags) g.split_flags += moe::kSplitSlots;  // the down launch's flag bank
   g.A = H;
   g.K = c.F;
   g.N = c.D;
@@ -256,6 +263,11 @@ hipError_t run_shared(const moe_cfg& c, const void* x, const moe_weights& w, voi
 extern "C" {
 
 int moe_version(void) { return MOE_ABI_VERSION; }
+
+int moe_set_split_wait(int polls) {
+  if (polls < 0) return MOE_ERR_INVALID_ARG;
+  return g_split_wait.exchange(polls);
+}
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
     tilemap[2 + 2 * (base + i)] = start + i * bm;
   }
   if (e == 1023) tilemap[0] = base + nt;
-  if (flags && e < kSplitSlots) flags[e] = 0;
+  if (flags && e < 2 * kSplitSlots) flags[e] = 0;  // both banks
 }
 
 // expert of a segment row: the last e with offsets[e] <= r

@@ -111,7 +111,9 @@ __device__ __forceinline__ void finish_tile16(const Args& a, const Job& jb, f32x
                                               int n0) {
   const int wm = wave >> 2, wn = wave & 3, l16 = lane & 15, g = lane >> 4;
   const int row0 = jb.row0, row_end = jb.row_end, N = a.N;
-  // ---- split tiles: partial sums through the workspace (float4 q = 4 i + j)
+  // ---- split tiles: partial sums through the workspace (float4 q = 4 i + j);
+  // a wave that lost a part stores NaN
+  bool lost = false;
   if (jb.S > 1 && !split_exchange(
                       a, jb,
                       [&](int q) {
@@ -125,7 +127,7 @@ __device__ __forceinline__ void finish_tile16(const Args& a, const Job& jb, f32x
                         t[2] += v.z;
                         t[3] += v.w;
                       },
-                      wave, lane, tid))
+                      wave, lane, tid, lost))
     return;
 
   // ---- epilogue through LDS (16-byte global stores). Accumulator r of lane
@@ -150,7 +152,8 @@ __device__ __forceinline__ void finish_tile16(const Args& a, const Job& jb, f32x
           }
           // SiLU(g) u with the hardware exp2 and reciprocal and the hardware
           // round-to-nearest-even bf16 conversion
-          const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          if (lost) h = __builtin_nanf("");
           *reinterpret_cast<__bf16*>(wl + m * 64 + (16 * j + l16) * 2) = (__bf16)h;
         }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own wave's tile only
@@ -175,7 +178,8 @@ __device__ __forceinline__ void finish_tile16(const Args& a, const Job& jb, f32x
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int m = 16 * i + 4 * g + r;
-            *reinterpret_cast<float*>(wl + m * 128 + (16 * jj + l16) * 4) = acc[i][2 * hh + jj][r];
+            *reinterpret_cast<float*>(wl + m * 128 + (16 * jj + l16) * 4) =
+                lost ? __builtin_nanf("") : acc[i][2 * hh + jj][r];
           }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -755,6 +759,7 @@ hipError_t launch_gemm16(const GemmProblem& p, bool swiglu, hipStream_t s) {
   a.n_tiles_n = swiglu ? ceil_div(p.N, 128) : ceil_div(p.N, 256);
   a.split_ws = p.split_ws;
   a.split_flags = p.split_flags;
+  a.split_wait = p.split_wait;
   a.B0 = p.B0;
   a.B1 = p.B1;
   a.clamp = p.clamp;

@@ -420,7 +420,8 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
 #undef A8_HALF
 #undef A8_MF
 
-  if (jb.S > 1 && !split_exchange(a, jb, acc, wave, lane, tid)) return;
+  bool lost = false;  // a wave that lost a split part stores NaN
+  if (jb.S > 1 && !split_exchange(a, jb, acc, wave, lane, tid, lost)) return;
 
   __syncthreads();  // every wave is done with the operand stages
   if (MODE == MODE_SWIGLU) {
@@ -459,7 +460,12 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
         v[4 * cc + 3] = w4.w;
       }
       uint32_t q[8];
-      const uint32_t s = mxfp8_block(v, q);
+      uint32_t s = mxfp8_block(v, q);
+      if (lost) {  // e4m3 NaN codes and the e8m0 NaN scale
+        s = 0xFFu;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = 0x7F7F7F7Fu;
+      }
       if (grow < row_end && f0 < N) {
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(Hc + (size_t)grow * N + f0);
         dst[0] = u32x4_t{q[0], q[1], q[2], q[3]};
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
       }
     }
   } else {
-    store_down_tile(a, acc, smem, wave, lane, row0 + 128 * wm, row_end, n0, bcol);
+    store_down_tile(a, acc, smem, wave, lane, row0 + 128 * wm, row_end, n0, bcol, lost);
   }
 }
 
@@ -501,6 +507,7 @@ hipError_t launch_gemm_a8(const GemmProblem& p, bool swiglu, hipStream_t s) {
   a.n_tiles_n = swiglu ? ceil_div(p.N, 128) : ceil_div(p.N, 256);
   a.split_ws = p.split_ws;
   a.split_flags = p.split_flags;
+  a.split_wait = p.split_wait;
   a.B0 = p.B0;
   a.B1 = p.B1;
   a.S0 = p.S0;

@@ -43,7 +43,8 @@ struct Args {
   float clamp;
   void* out;
   float* split_ws;       // partial accumulators of split tiles, or nullptr
-  int32_t* split_flags;  // one ready flag per partial slot, zero between launches
+  int32_t* split_flags;  // one ready flag per partial slot, zero before the launch
+  int split_wait;        // polls of a ready flag before a split tile gives up
 };
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -173,9 +174,21 @@ __device__ __forceinline__ bool schedule_tile(const Args& a, int b, Job& j) {
 // adds v to it. Parts 0..S-2 store theirs, raise their flag and return
 // false; part S-1 adds the others' in part order and returns true (it runs
 // the epilogue).
+//
+// Part S-1 is the highest workgroup index of its tile, so the parts it
+// waits for were dispatched before it (the dispatcher hands out workgroups
+// in index order) and never wait themselves: their flags rise within their
+// run time. Each wave polls a flag itself (all lanes one address, so one
+// request per poll), at most a.split_wait times. A wave whose flag does not
+// rise in time sets `lost` and adds nothing from that slot; the epilogue
+// then stores NaN for the wave's outputs, so a broken hand-off shows up as
+// NaN, never as a plausible partial sum. Flags are not reset here: the
+// gate/up and down launches of one layer use separate flag banks, both
+// zeroed by the tile-map kernel before the gate/up launch, so a flag that
+// rises after its consumer gave up cannot mislead a later launch.
 template <class Get, class Add>
 __device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, Get get, Add add,
-                                               int wave, int lane, int tid) {
+                                               int wave, int lane, int tid, bool& lost) {
   const int S = jb.S, part = jb.part, slot0 = jb.slot0;
   float4* mine = reinterpret_cast<float4*>(a.split_ws) + wave * 32 * 64 + lane;
   if (part < S - 1) {
@@ -190,20 +203,21 @@ __device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, Get
     }
     return false;
   }
+  lost = false;
   for (int p = 0; p < S - 1; ++p) {
-    if (tid == 0) {
-      // bounded wait: the part was dispatched before this workgroup and
-      // never waits itself, so the flag rises within its run time
-      for (int spin = 0; spin < (1 << 24); ++spin) {
-        if (__hip_atomic_load(a.split_flags + slot0 + p, __ATOMIC_ACQUIRE,
-                              __HIP_MEMORY_SCOPE_AGENT) != 0)
-          break;
-        __builtin_amdgcn_s_sleep(2);
+    const int32_t* flag = a.split_flags + slot0 + p;
+    bool up = false;
+    for (int n = 0; n < a.split_wait; ++n) {
+      if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        up = true;
+        break;
       }
-      __hip_atomic_store(a.split_flags + slot0 + p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_sleep(2);
     }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!up) {
+      lost = true;
+      continue;
+    }
     const float4* src = mine + (size_t)(slot0 + p) * (TM * TN / 4);
 #pragma unroll
     for (int q = 0; q < 32; ++q) add(q, src[q * 64]);
@@ -214,7 +228,7 @@ __device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, Get
 // split_exchange for the 32x32 accumulator layout acc[4][2] (f32x16):
 // float4 q = 4 (2i + j) + r/4 holds acc[i][j][r..r+3]
 __device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, f32x16_t (&acc)[4][2],
-                                               int wave, int lane, int tid) {
+                                               int wave, int lane, int tid, bool& lost) {
   return split_exchange(
       a, jb,
       [&](int q) {
@@ -230,17 +244,19 @@ __device__ __forceinline__ bool split_exchange(const Args& a, const Job& jb, f32
         t[r + 2] += v.z;
         t[r + 3] += v.w;
       },
-      wave, lane, tid);
+      wave, lane, tid, lost);
 }
 
 // Down-projection epilogue: the wave's 128 rows x 64 fp32 columns (rows
 // from wrow0, B-columns n0 + bcol[j] + 0..31) go through the wave's 16 KB of
 // LDS at wl, in two halves of 32 columns, so that the global stores are
-// 16 bytes per lane. Accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-// column l%32 of its 32x32 tile.
+// 16 bytes per lane; NaN instead when the wave lost a split part.
+// Accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 of
+// its 32x32 tile.
 __device__ __forceinline__ void store_down_tile(const Args& a, const f32x16_t (&acc)[4][2],
                                                 unsigned char* smem, int wave, int lane, int wrow0,
-                                                int row_end, int n0, const int (&bcol)[2]) {
+                                                int row_end, int n0, const int (&bcol)[2],
+                                                bool lost) {
   const int lrow = lane & 31, lq = lane >> 5, N = a.N;
   unsigned char* wl = smem + wave * (128 * 128);
   float* Y = static_cast<float*>(a.out);
@@ -251,7 +267,8 @@ __device__ __forceinline__ void store_down_tile(const Args& a, const f32x16_t (&
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 32 * i + 8 * (r >> 2) + 4 * lq + (r & 3);
-        *reinterpret_cast<float*>(wl + m * 128 + lrow * 4) = acc[i][j][r];
+        *reinterpret_cast<float*>(wl + m * 128 + lrow * 4) =
+            lost ? __builtin_nanf("") : acc[i][j][r];
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll

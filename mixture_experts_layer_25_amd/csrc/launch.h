@@ -26,10 +26,14 @@ inline int max_mtiles(const moe_cfg& c) { return ceil_div((long long)c.T * c.top
 inline size_t tilemap_ints(const moe_cfg& c) { return 1 + 2 * (size_t)max_mtiles(c); }
 // The grouped GEMMs split the tiles of their last round along K: one slot
 // of 256 x 256 fp32 partial sums per split part (at most 32 per XCD), and
-// one ready flag per slot.
+// one ready flag per slot in each of two banks (gate/up, then down), both
+// zeroed by the tile-map kernel.
 constexpr int kSplitSlots = 256;
 constexpr size_t kSplitSlotBytes = 256 * 256 * 4;
-constexpr size_t kSplitFlagBytes = 1024;
+constexpr size_t kSplitFlagBytes = 2 * kSplitSlots * 4;
+// Default polls of a split part's ready flag before its consumer gives up
+// (each poll sleeps about 128 cycles: about a second in all).
+constexpr int kSplitWaitDefault = 1 << 24;
 inline bool gemm_splits(const moe_cfg& c) { return c.act_dtype == MOE_BF16; }
 inline size_t split_bytes(const moe_cfg& c) {
   return gemm_splits(c) ? kSplitFlagBytes + kSplitSlots * kSplitSlotBytes : 0;
@@ -45,8 +49,8 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
                            int32_t* chunk_ws, hipStream_t s);
 
 // Builds the tile map (tilemap_ints(c) int32, M-tiles of kBM rows)
-// from device offsets.
-// also zeroes the kSplitSlots split flags when `flags` is not null.
+// from device offsets; also zeroes both banks of split flags
+// (2 kSplitSlots int32) when `flags` is not null.
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
                           int32_t* flags, hipStream_t s);
 
@@ -73,6 +77,7 @@ struct GemmProblem {
                            // grouped scales [ceil(N/512)][rows][16]); down: fp32 [rows][N]
   float* split_ws;         // kSplitSlots partial-sum slots, or nullptr: no split
   int32_t* split_flags;    // kSplitSlots flags, zero before the launch
+  int split_wait;          // polls of a flag before a split tile stores NaN
 };
 hipError_t launch_gemm_swiglu(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_down(const GemmProblem& p, hipStream_t s);

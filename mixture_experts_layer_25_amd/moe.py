@@ -52,7 +52,7 @@ _lib = None
 SYMBOLS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down",
            "moe_shared_expert", "moe_combine", "moe_forward", "moe_quantize_mxfp8",
-           "moe_status_string", "moe_last_hip_error", "moe_version"]
+           "moe_status_string", "moe_last_hip_error", "moe_version", "moe_set_split_wait"]
 
 
 def lib():
@@ -80,6 +80,8 @@ def lib():
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_last_hip_error.restype = ctypes.c_int
     L.moe_version.restype = ctypes.c_int
+    L.moe_set_split_wait.restype = ctypes.c_int
+    L.moe_set_split_wait.argtypes = [ctypes.c_int]
     for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
                  "moe_expert_gate_up", "moe_expert_down", "moe_shared_expert", "moe_combine",
                  "moe_forward", "moe_quantize_mxfp8"):
@@ -259,3 +261,12 @@ def forward(cfg: Cfg, x, W_r, bias, weights: Weights, y=None, ws=None, topk_idx=
                              _p(y), _p(topk_idx), _p(topk_w), _p(counts), _p(offsets), _p(ws),
                              ws.numel(), _stream(stream)))
     return y
+
+
+def set_split_wait(polls: int) -> int:
+    """moe_set_split_wait: polls of a split GEMM tile's ready flags before it
+    stores NaN (process-wide); returns the previous value."""
+    r = lib().moe_set_split_wait(int(polls))
+    if r < 0:
+        _check(r)
+    return r

@@ -18,9 +18,10 @@ Recipe (every tensor, every config):
   consecutive elements along the reduction dimension K) are quantised from the
   float32 draw: for each 32-block, X = 2^(floor(log2(amax)) - 2), each element
   v/X is rounded to the nearest e2m1 value with ties to the even code and
-  saturated at +-6; an all-zero block gets scale code 0. Codes are stored
-  K-contiguous per output column: ``codes uint8[E][N][K/2]`` (element 2i in the
-  low nibble), ``scales uint8[E][N][K/32]``.
+  saturated at +-6; an all-zero block gets scale code 0. Codes are stored by
+  32-element K-blocks, block-major: ``codes uint8[E][K/32][N][16]`` (the 16
+  bytes of block b of column n, element 2i of the block in the low nibble of
+  byte i), ``scales uint8[E][K/32][N]``.
 
 The five named workloads and their shapes come from the layer description:
 a tiny fp32 top-2 layer, the Mixtral shape (8 experts, top-2, F=14336), a

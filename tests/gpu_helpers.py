@@ -45,6 +45,33 @@ def sample_tokens(cfg: syn.Config, slot_pos: np.ndarray, n: int = 32, seed: int 
     return np.array(sorted(picks), np.int32)
 
 
+def stratified_tokens(cfg: syn.Config, idx: np.ndarray, slot_pos: np.ndarray,
+                      perm: np.ndarray, offsets: np.ndarray, n: int = 32,
+                      seed: int = 7) -> np.ndarray:
+    """Tokens whose y the full-size tests compare with the oracle: those of
+    sample_tokens, then greedily tokens that add kept experts not yet covered
+    until every expert with a kept pair appears, and one row (its token) of
+    every M-tile that holds a tile split along K in either GEMM."""
+    import tile_plan as tp
+    picks = set(sample_tokens(cfg, slot_pos, n, seed).tolist())
+    kept = slot_pos >= 0
+    need = set(np.unique(idx[kept]).tolist())
+    for t in picks:
+        need -= set(idx[t][kept[t]].tolist())
+    gain = [set(idx[t][kept[t]].tolist()) for t in range(cfg.T)]
+    while need:
+        t = max(range(cfg.T), key=lambda u: len(gain[u] & need))
+        picks.add(t)
+        need -= gain[t]
+    if cfg.act != syn.F32:
+        for swiglu in (True, False):
+            K, N = (cfg.D, cfg.F) if swiglu else (cfg.F, cfg.D)
+            for t in tp.plan(offsets, K, N, swiglu):
+                if t.S > 1:
+                    picks.add(int(perm[t.row0]))
+    return np.array(sorted(picks), np.int32)
+
+
 def gpu_forward(inp: syn.Inputs, stagewise: bool = False):
     """Run the layer on the GPU; returns host numpy results."""
     cfg, x, W_r, bias, w = upload.to_device(inp)

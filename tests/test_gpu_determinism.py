@@ -11,11 +11,12 @@ import pytest
 import torch
 
 from mixture_experts_layer_25_amd import moe, synthetic as syn, upload
+from split_cases import SPLIT_CASES
 
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # small shapes: every XCD gets one partial round, tiles are split up to 8 ways
+    # small shapes (K < 2048: no tile is split along K)
     "mixtral_small": syn.small_variant(syn.CONFIGS["mixtral"], T=300, D=256, F=352),
     "fine384_small": syn.small_variant(syn.CONFIGS["fine384_mxfp4"], T=200, D=256, F=128),
     "capacity_small": syn.small_variant(syn.CONFIGS["capacity"], T=500, D=256, F=160),
@@ -23,6 +24,9 @@ CASES = {
     # full Mixtral shape: the down GEMM's last round is split 4 ways
     "mixtral": syn.CONFIGS["mixtral"],
 }
+# small shapes whose tiles are split along K in 2, 4 and 8 parts (the host
+# replica of the schedule checks that they split)
+CASES.update({n: c for n, (c, _) in SPLIT_CASES.items()})
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -12,7 +12,7 @@ import torch
 import oracle
 from mixture_experts_layer_25_amd import moe, synthetic as syn, upload
 from gpu_helpers import (act_to_f64, assert_close, check_routing, gpu_forward, sample_tokens,
-                         tol_for)
+                         stratified_tokens, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,22 +81,41 @@ def test_small_fused_equals_stagewise(name):
 @pytest.mark.parametrize("name", syn.CONFIG_ORDER + ["fine384_mxfp4_a8"])
 def test_full_size(name):
     """Full workload, in the launch configuration the benchmark times:
-    routing and dispatch on every token, y on sampled tokens."""
+    routing on every token; dispatch (counts, offsets, slot positions with
+    the drop decisions, perm_token) bit for bit on every pair, from a
+    full-size moe_dispatch of the forward's own indices; y on a sample of
+    tokens that covers every expert and a row of every M-tile with a tile
+    split along K."""
     cfg = syn.CONFIGS[name]
     print(f"[parity] full {name}: generating", flush=True)
     inp = syn.make_inputs(cfg)
     print(f"[parity] full {name}: gpu", flush=True)
-    got = gpu_forward(inp, stagewise=False)
+    c, x, W_r, bias, w = upload.to_device(inp)
+    dev = x.device
+    idx_d = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    tw_d = torch.empty(idx_d.shape, dtype=torch.float32, device=dev)
+    cnt_d = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    off_d = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    y = moe.forward(c, x, W_r, bias, w, topk_idx=idx_d, topk_w=tw_d, counts=cnt_d,
+                    offsets=off_d)
+    d = moe.dispatch(c, idx_d, x)
+    torch.cuda.synchronize()
+    got = dict(idx=idx_d.cpu().numpy(), w=tw_d.cpu().numpy(), counts=cnt_d.cpu().numpy(),
+               offsets=off_d.cpu().numpy(), slot_pos=d["slot_pos"].cpu().numpy(),
+               perm=d["perm"].cpu().numpy(), y=upload.to_host_bits(y)[:cfg.T])
+    del d, y
     print(f"[parity] full {name}: oracle routing", flush=True)
-    logits, idx, w = oracle.route(cfg, inp.x, inp.W_r, inp.bias)
+    logits, idx, w_ref = oracle.route(cfg, inp.x, inp.W_r, inp.bias)
     counts, offsets, slot_pos, perm = oracle.dispatch(cfg, idx)
-    ref = dict(idx=idx, w=w, counts=counts, offsets=offsets)
+    ref = dict(idx=idx, w=w_ref, counts=counts, offsets=offsets, slot_pos=slot_pos, perm=perm)
     check_routing(cfg, got, ref)
+    n_drop = int((slot_pos < 0).sum())
     if cfg.capacity > 0:
-        assert (slot_pos < 0).any(), "capacity workload should drop pairs"
-    toks = sample_tokens(cfg, slot_pos, n=32 if cfg.T > 64 else cfg.T)
-    print(f"[parity] full {name}: oracle y on {len(toks)} tokens", flush=True)
-    y_exact, y_ref = oracle.forward_tokens(inp, idx, w, slot_pos, toks)
+        assert n_drop > 0, "capacity workload should drop pairs"
+    toks = stratified_tokens(cfg, idx, slot_pos, perm, offsets, n=32 if cfg.T > 64 else cfg.T)
+    print(f"[parity] full {name}: {n_drop} drops bit-exact; oracle y on {len(toks)} tokens",
+          flush=True)
+    y_exact, y_ref = oracle.forward_tokens(inp, idx, w_ref, slot_pos, toks)
     err = assert_close(got["y"][toks], y_ref, tol_for(cfg), f"{name} y")
     print(f"[parity] full {name}: counts min {counts.min()} max {counts.max()} "
           f"kept {offsets[-1]} of {cfg.T * cfg.k}; max rel err {err:.3g}", flush=True)
