@@ -88,7 +88,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or mode */
   MOE_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
   MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than needed */
-  MOE_ERR_HIP = -4           /* a HIP launch failed */
+  MOE_ERR_HIP = -4,          /* a HIP launch failed */
+  MOE_ERR_SCRATCH = -5       /* size beyond the fixed scratch of moe_dispatch_noalloc */
 } moe_status;
 
 typedef enum {
@@ -166,6 +167,20 @@ int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* 
 int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
                  int32_t* offsets, int32_t* slot_pos, int32_t* perm_token, void* x_perm,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the per-chunk expert
+ * counts in a fixed 1 MiB device array of the library instead of a
+ * caller's workspace. Limit: E * ceil(T / 256) <= 262144 (e.g. E = 1024
+ * with T up to 65536), else MOE_ERR_SCRATCH and nothing is enqueued. It
+ * calls no allocating routine. Each GPU holds its own copy of the array
+ * until the process ends, and every call on that GPU shares it: calls that
+ * overlap on one GPU (other streams, other threads) race. Nothing in it
+ * needs clearing between calls. */
+int moe_dispatch_noalloc(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
+                         int32_t* counts, int32_t* offsets, int32_t* slot_pos,
+                         int32_t* perm_token, void* x_perm, void* stream);
 
 /* Routed experts ("FFN, SwiGLU and MoE" sec. 2; "ops-transformer"
  * optimisation 3, one launch over all experts' irregular segments):

@@ -278,6 +278,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "beyond the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -319,6 +320,24 @@ int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int
   return hip_status(moe::launch_dispatch(*cfg, topk_idx, x, counts, offsets, slot_pos, perm_token,
                                          x_perm, static_cast<int32_t*>(ws),
                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch_noalloc(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
+                         int32_t* counts, int32_t* offsets, int32_t* slot_pos,
+                         int32_t* perm_token, void* x_perm, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!dev_ok(topk_idx) || !dev_ok(x) || !dev_ok(counts) || !dev_ok(offsets) ||
+      !dev_ok(slot_pos) || !dev_ok(perm_token) || !dev_ok(x_perm))
+    return MOE_ERR_INVALID_ARG;
+  if ((size_t)cfg->E * moe::num_chunks(*cfg) > moe::kDispatchScratchInts)
+    return MOE_ERR_SCRATCH;
+  if (cfg->T == 0) return MOE_OK;
+  int32_t* scratch = nullptr;
+  hipError_t e = moe::dispatch_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(moe::launch_dispatch(*cfg, topk_idx, x, counts, offsets, slot_pos, perm_token,
+                                         x_perm, scratch, static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,

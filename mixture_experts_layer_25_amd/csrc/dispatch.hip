@@ -23,6 +23,8 @@
 //          (MOE_MXFP4_A8) the wave quantises the row once instead and writes
 //          the codes to each kept slot's row, the scales in the grouped
 //          layout of the A8 GEMM after the codes.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "mxfp8.h"
@@ -237,6 +239,34 @@ __global__ __launch_bounds__(256) void dispatch_copy_mxfp8_kernel(
 }
 
 }  // namespace
+
+// Scratch of the no-allocation dispatch (moe_dispatch_noalloc): the
+// per-chunk expert counts, int32 [E][ceil(T/256)], at most
+// kDispatchScratchInts. The count kernel writes every entry it uses, so
+// nothing needs clearing between calls. Every call on a device shares that
+// device's copy; calls that overlap on one device race.
+static __device__ __align__(256) int32_t scratch[kDispatchScratchInts];
+
+hipError_t dispatch_scratch(int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    // the device address of this device's copy; the host-side name of the
+    // array is not a device address
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,

@@ -43,6 +43,12 @@ inline int num_chunks(const moe_cfg& c) { return ceil_div(c.T, kChunk); }
 hipError_t launch_router(const moe_cfg& c, const void* x, const float* W_r, const float* bias,
                          int32_t* idx, float* w, float* logits, hipStream_t s);
 
+// int32 entries of the fixed device scratch of moe_dispatch_noalloc (1 MiB)
+constexpr size_t kDispatchScratchInts = 1 << 18;
+// Device address of the current device's dispatch scratch (resolved on the
+// first call on each device).
+hipError_t dispatch_scratch(int32_t** out);
+
 // chunk_ws: int32 [E][num_chunks]
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,

@@ -52,7 +52,8 @@ _lib = None
 SYMBOLS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down",
            "moe_shared_expert", "moe_combine", "moe_forward", "moe_quantize_mxfp8",
-           "moe_status_string", "moe_last_hip_error", "moe_version", "moe_set_split_wait"]
+           "moe_status_string", "moe_last_hip_error", "moe_version", "moe_set_split_wait",
+           "moe_dispatch_noalloc"]
 
 
 def lib():
@@ -69,6 +70,7 @@ def lib():
     L.moe_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_ffn.argtypes = [P, vp, vp, W, vp, vp, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [P, vp, vp, W, vp, vp, sz, vp]
     L.moe_expert_down.argtypes = [P, vp, vp, W, vp, vp, sz, vp]
@@ -82,7 +84,8 @@ def lib():
     L.moe_version.restype = ctypes.c_int
     L.moe_set_split_wait.restype = ctypes.c_int
     L.moe_set_split_wait.argtypes = [ctypes.c_int]
-    for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
+    for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_dispatch_noalloc",
+                 "moe_expert_ffn",
                  "moe_expert_gate_up", "moe_expert_down", "moe_shared_expert", "moe_combine",
                  "moe_forward", "moe_quantize_mxfp8"):
         getattr(L, name).restype = ctypes.c_int
@@ -183,6 +186,15 @@ def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None):
                               _p(slot_pos), _p(perm), _p(x_perm), _p(ws), ws.numel(),
                               _stream(stream)))
     return dict(counts=counts, offsets=offsets, slot_pos=slot_pos, perm=perm, x_perm=x_perm)
+
+
+def dispatch_noalloc(cfg: Cfg, topk_idx, x, counts, offsets, slot_pos, perm, x_perm,
+                     stream=None):
+    """moe_dispatch_noalloc: moe_dispatch into caller-allocated outputs, with
+    the library's fixed device scratch instead of a workspace."""
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts),
+                                      _p(offsets), _p(slot_pos), _p(perm), _p(x_perm),
+                                      _stream(stream)))
 
 
 def expert_ffn(cfg: Cfg, x_perm, offsets, weights: Weights, H=None, y_perm=None, ws=None,
