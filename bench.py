@@ -66,15 +66,19 @@ def parse():
 
 
 def algorithmic(cfg, A):
-    """Algorithmic work of one forward (what the method must compute/move)."""
+    """Algorithmic work of one forward (what the method must compute/move).
+    With bf16 activations dispatch copies no rows (the gate/up GEMM gathers
+    them from x), so its bytes are the indices alone: topk_idx read,
+    slot_pos and perm_token written."""
     sx = 2 if cfg.act == 1 else 4
     T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
+    rows = 0 if cfg.act == 1 else T * D * sx + A * D * sx
     return dict(
         gate_up_flop=4.0 * D * F * A,
         down_flop=2.0 * D * F * A,
         shared_flop=6.0 * D * cfg.shared_F * T,
         route_bytes=T * D * sx + D * E * 4 + T * k * 8,
-        dispatch_bytes=T * k * 8 + T * D * sx + A * D * sx + A * 4,
+        dispatch_bytes=T * k * 8 + A * 4 + rows,
         combine_bytes=A * D * 4 + T * k * 8 + T * D * sx + (T * D * 4 if cfg.shared_F else 0),
     )
 
@@ -141,8 +145,19 @@ def find_one(d, suffix):
     return hits[0]
 
 
+def _arg_of(command, flag, default):
+    m = re.search(re.escape(flag) + r"[ =](\d+)", command)
+    return int(m.group(1)) if m else default
+
+
 def summarize_trace(run_dir, workload, command):
-    """rocprofv3 --kernel-trace --stats output -> profiles/kernel_trace_<workload>.txt"""
+    """rocprofv3 --kernel-trace --stats output -> profiles/kernel_trace_<workload>.txt:
+    every kernel's statistics over all its dispatches, and for the roofline
+    kernel the mean over the dispatches of the two timed passes of the
+    benchmark (in launch order: W warm-up and K timed moe_forward steps, then
+    max(1, W/2) warm-up and K timed stage-by-stage steps), the second of which
+    is the live figure the benchmark reports."""
+    from mixture_experts_layer_25_amd import synthetic as syn
     rows = read_csv(find_one(run_dir, "kernel_stats.csv"))
     out = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.txt")
     lines = [f"# rocprofv3 kernel-trace summary, workload {workload}",
@@ -153,6 +168,20 @@ def summarize_trace(run_dir, workload, command):
         lines.append(f"{short_name(r['Name']):90s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                      f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    rk = roofline_kernel(syn.CONFIGS[workload])["name"]
+    K = _arg_of(command, "--steps", 50)
+    W = _arg_of(command, "--warmup", 10)
+    disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                  for r in read_csv(find_one(run_dir, "kernel_trace.csv"))
+                  if short_name(r["Kernel_Name"]) == rk)
+    dur = [(e - s) / 1e3 for s, e in disp]
+    w2 = max(1, W // 2)
+    fused = dur[W:W + K]
+    stage = dur[W + K + w2:W + K + w2 + K]
+    if len(dur) >= W + K + w2 + K:
+        lines.append(f"# {rk}: {len(dur)} dispatches; mean of the {K} timed moe_forward steps "
+                     f"{sum(fused) / K:.2f} us, of the {K} timed stage-by-stage steps (the "
+                     f"benchmark's live roofline figure) {sum(stage) / K:.2f} us")
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
 
@@ -396,15 +425,18 @@ def main():
 
     # The timed steps are moe_forward itself. A second pass runs the layer
     # through its stage entry points (the same kernels moe_forward launches,
-    # in the same order, on the same stream; with bf16 activations plus the
-    # dispatch copy that the fused layer's gather makes unnecessary), with a
-    # HIP event between stages, so that each stage's duration is known.
+    # in the same order, on the same stream, the gate/up GEMM gathering its
+    # rows from x as in moe_forward), with a HIP event between stages, so
+    # that each stage's duration is known.
     d_ws = moe.workspace(c, moe.WS_DISPATCH, dev)
     f_ws = moe.workspace(c, moe.WS_EXPERT_FFN, dev)
     tk = T * k
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
     perm = torch.empty(tk, dtype=torch.int32, device=dev)
-    x_perm = torch.empty((tk, cfg.D), dtype=moe.act_torch_dtype(c), device=dev)
+    # bf16 activations: as in moe_forward, dispatch copies no rows and the
+    # gate/up GEMM gathers them from x through perm
+    gathered = cfg.act == syn.BF16
+    x_perm = None if gathered else torch.empty((tk, cfg.D), dtype=moe.act_torch_dtype(c), device=dev)
     H = torch.empty((tk, cfg.F), dtype=moe.act_torch_dtype(c), device=dev)
     y_perm = torch.empty((tk, cfg.D), dtype=torch.float32, device=dev)
     Hs = ys = None
@@ -423,11 +455,15 @@ def main():
                                      idx.data_ptr(), tw.data_ptr(), None, sp),
         "dispatch": lambda: L.moe_dispatch(P(c), idx.data_ptr(), x.data_ptr(), counts.data_ptr(),
                                            offsets.data_ptr(), slot_pos.data_ptr(),
-                                           perm.data_ptr(), x_perm.data_ptr(), d_ws.data_ptr(),
-                                           d_ws.numel(), sp),
-        "gate_up": lambda: L.moe_expert_gate_up(P(c), x_perm.data_ptr(), offsets.data_ptr(),
-                                                P(wstruct), H.data_ptr(), f_ws.data_ptr(),
-                                                f_ws.numel(), sp),
+                                           perm.data_ptr(),
+                                           None if gathered else x_perm.data_ptr(),
+                                           d_ws.data_ptr(), d_ws.numel(), sp),
+        "gate_up": (lambda: L.moe_expert_gate_up_gathered(
+                        P(c), x.data_ptr(), perm.data_ptr(), offsets.data_ptr(), P(wstruct),
+                        H.data_ptr(), f_ws.data_ptr(), f_ws.numel(), sp)) if gathered else
+                   (lambda: L.moe_expert_gate_up(P(c), x_perm.data_ptr(), offsets.data_ptr(),
+                                                 P(wstruct), H.data_ptr(), f_ws.data_ptr(),
+                                                 f_ws.numel(), sp)),
         "down": lambda: L.moe_expert_down(P(c), H.data_ptr(), offsets.data_ptr(), P(wstruct),
                                           y_perm.data_ptr(), f_ws.data_ptr(), f_ws.numel(), sp),
         "combine": lambda: L.moe_combine(P(c), y_perm.data_ptr(), slot_pos.data_ptr(),
@@ -491,6 +527,8 @@ def main():
     s1.record(stream)
     torch.cuda.synchronize()
     stagewise_ms = s0.elapsed_time(s1) / args.steps
+    stage_roof = [evs[order.index("gate_up")].elapsed_time(evs[order.index("gate_up") + 1])
+                  for evs in ev]
     stage_ms = {n: sum(evs[i].elapsed_time(evs[i + 1]) for evs in ev) / args.steps
                 for i, n in enumerate(order)}
     log(f"[bench] stage by stage: {stagewise_ms:.3f} ms/step")
@@ -500,9 +538,12 @@ def main():
     # previous stage left there; the stage is timed alone
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
     nfl = min(args.steps, 10)
-    fl_ms = {n: 0.0 for n in order}
+    mem_bound = ("route", "dispatch", "combine")
+    fl_ms = {n: 0.0 for n in mem_bound}
     for _ in range(nfl):
         for n, fn in zip(order, fns):
+            if n not in mem_bound:
+                continue
             flush.zero_()
             a0, a1 = new_event(), new_event()
             a0.record(stream)
@@ -599,12 +640,63 @@ def main():
         "grouped_gemm_frac_of_bf16_peak": gemm_tf / PEAK_BF16_TFLOPS,
         "stages": stage_report,
         "stages_mall_flushed": flushed,
-        "env": {"device": torch.cuda.get_device_name(dev), "hip": torch.version.hip,
-                "torch": torch.__version__, "cus": torch.cuda.get_device_properties(dev).multi_processor_count},
+        "env": environment(torch, dev),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def _smi(*args):
+    """rocm-smi's JSON answer for one card (empty if the tool is missing)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", *args, "--json"], capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout or "{}")
+    except Exception:
+        return {}
+    cards = [v for kk, v in d.items() if kk.startswith("card")]
+    return {**(cards[0] if cards else {}), **d.get("system", {})}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def environment(torch, dev):
+    """Device, clocks (as rocm-smi reports them after the timed work),
+    driver and software versions, host CPU."""
+    p = torch.cuda.get_device_properties(dev)
+    clocks = _smi("--showclocks")
+    drv = _smi("--showdriverversion")
+    return {"device": torch.cuda.get_device_name(dev), "arch": getattr(p, "gcnArchName", ""),
+            "cus": p.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
+            "gpu_clocks": {kk: v for kk, v in clocks.items() if "clock" in kk.lower()},
+            "driver": {kk: v for kk, v in drv.items() if "driver" in kk.lower()},
+            "host_cpu": cpu_model(), "host_threads": os.cpu_count()}
+
+
+def _tiny_single_thread():
+    """The oracle on the whole tiny fp32 layer (T = 64) with one thread, in a
+    child process (its OpenMP runtime then starts with one thread)."""
+    import subprocess
+    code = ("import time, oracle; from mixture_experts_layer_25_amd import synthetic as syn; "
+            "inp = syn.make_inputs(syn.CONFIGS['tiny_fp32']); oracle.forward(inp); "
+            "t = time.perf_counter(); [oracle.forward(inp) for _ in range(5)]; "
+            "print((time.perf_counter() - t) / 5)")
+    env = {**os.environ, "OMP_NUM_THREADS": "1"}
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=300)
+    s = float(r.stdout.strip().splitlines()[-1])
+    return {"value": 64 / s, "unit": "tokens/s", "cores": 1, "seconds_per_layer": s,
+            "sample": "the whole tiny_fp32 layer (T=64, D=128, E=8, top-2, F=256), "
+                      "mean of 5 runs"}
 
 
 def cpu_baseline(cfg, seconds):
@@ -633,9 +725,13 @@ def cpu_baseline(cfg, seconds):
     n = max(n0, (n // n0) * n0)
     t = run(n) if n != n0 else t0
     log(f"[bench] cpu oracle: {n} tokens in {t:.2f}s on {threads} threads")
+    single = _tiny_single_thread()
+    log(f"[bench] cpu oracle, tiny fp32 layer, one thread: {single['value']:.0f} tokens/s")
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {n} tokens of the {cfg.name} workload as an {n}-token layer "
-                      f"(full route, dispatch, {cfg.k} SwiGLU experts per token, combine)"}
+                      f"(full route, dispatch, {cfg.k} SwiGLU experts per token, combine)",
+            "tiny_fp32_one_thread": single}
 
 
 if __name__ == "__main__":

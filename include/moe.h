@@ -137,7 +137,8 @@ typedef struct moe_weights {
  * MOE_WS_DISPATCH for moe_dispatch (per-chunk expert counts),
  * MOE_WS_EXPERT_FFN for moe_expert_ffn / _gate_up / _down (the device tile
  * map and, with bf16 activations, 64 MiB of fp32 partial sums plus two
- * banks of ready flags for the GEMM tiles that are split along K),
+ * banks of ready flags for the GEMM tiles that are split along K, and with
+ * MOE_MXFP4_A8 the MXFP8 copy of x that a gathered gate/up reads),
  * MOE_WS_FORWARD for moe_forward (all of the above plus H, y_perm, x_perm for fp32
  * activations only, the MXFP8 copy of x for MOE_MXFP4_A8 and, with a
  * shared expert, its H and output). A workspace carries state only within
@@ -163,6 +164,8 @@ int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* 
  * expert reaches cfg->capacity are dropped. Writes counts, offsets,
  * slot_pos, perm_token and copies each kept pair's x row to x_perm (with
  * MOE_MXFP4_A8: the row's MXFP8 quantisation, quantised once per token).
+ * x_perm may be NULL: then no row is copied (for callers that gather the
+ * rows through perm_token, as moe_expert_gate_up_gathered does).
  * Integer outputs are deterministic and bit-exact. */
 int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
                  int32_t* offsets, int32_t* slot_pos, int32_t* perm_token, void* x_perm,
@@ -201,6 +204,17 @@ int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* of
                        const moe_weights* w, void* H, void* ws, size_t ws_bytes, void* stream);
 int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
                     const moe_weights* w, float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_expert_gate_up reading its rows from x itself: routed row r is row
+ * perm_token[r] of x [T][D] ("ops-transformer" MoEForward gathers each
+ * expert's tokens; here the gather happens inside the GEMM's copies, so no
+ * dispatched copy x_perm is written). bf16 activations only
+ * (MOE_ERR_UNSUPPORTED otherwise); with MOE_MXFP4_A8 x is first quantised
+ * to MXFP8 once per token, into the workspace. The same kernels and
+ * results as moe_forward's gate/up stage. Workspace: MOE_WS_EXPERT_FFN. */
+int moe_expert_gate_up_gathered(const moe_cfg* cfg, const void* x, const int32_t* perm_token,
+                                const int32_t* offsets, const moe_weights* w, void* H, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* Shared expert ("DeepSeek-V4.1-Flash" sec. 1, 3): the same SwiGLU with
  * the bf16 weights Ws_* on every token. H_shared [T][shared_F] bf16 is

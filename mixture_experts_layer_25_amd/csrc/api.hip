@@ -95,15 +95,17 @@ struct Carver {
 size_t dispatch_ws(const moe_cfg& c) {
   return moe::align_up((size_t)c.E * moe::num_chunks(c) * 4, kAlign);
 }
-// expert FFN workspace: the tile map, then (bf16 weights) the split flags and
-// partial-sum slots of the grouped GEMMs
-size_t tilemap_bytes(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
-size_t ffn_ws(const moe_cfg& c) { return tilemap_bytes(c) + moe::split_bytes(c); }
 // MXFP8 copy of `rows` activation rows of width K: codes, then the scales
 // in the grouped layout the GEMM reads ([ceil(K/512)][rows][16])
 size_t mxfp8_bytes(size_t rows, int K) {
   return moe::align_up(rows * K, kAlign) + moe::align_up((size_t)((K + 511) / 512) * rows * 16, kAlign);
 }
+// expert FFN workspace: the tile map, then (bf16 activations) the split
+// flags and partial-sum slots of the grouped GEMMs, then (MXFP8 activations)
+// the MXFP8 copy of x that a gathered gate/up launch reads
+size_t tilemap_bytes(const moe_cfg& c) { return moe::align_up(moe::tilemap_ints(c) * 4, kAlign); }
+size_t xq_bytes(const moe_cfg& c) { return is_a8(c) ? mxfp8_bytes(c.T, c.D) : 0; }
+size_t ffn_ws(const moe_cfg& c) { return tilemap_bytes(c) + moe::split_bytes(c) + xq_bytes(c); }
 int32_t* split_flags_of(const moe_cfg& c, int32_t* tilemap) {
   if (!moe::gemm_splits(c)) return nullptr;
   return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tilemap) + tilemap_bytes(c));
@@ -113,12 +115,15 @@ float* split_ws_of(const moe_cfg& c, int32_t* tilemap) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(split_flags_of(c, tilemap)) +
                                   moe::kSplitFlagBytes);
 }
+uint8_t* xq_of(const moe_cfg& c, int32_t* tilemap) {
+  if (!is_a8(c)) return nullptr;
+  return reinterpret_cast<uint8_t*>(tilemap) + tilemap_bytes(c) + moe::split_bytes(c);
+}
 
 struct ForwardWs {
   int32_t *idx, *counts, *offsets, *slot_pos, *perm, *chunk_ws, *tilemap;
   float *w, *y_perm, *y_shared;
   void *x_perm, *H, *H_shared;
-  uint8_t* xq;  // MXFP8 copy of x (MXFP8 activations)
   size_t bytes;
 };
 
@@ -136,7 +141,6 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   f.tilemap = static_cast<int32_t*>(cv.take(ffn_ws(c)));
   // bf16: gate/up gathers its rows from x through perm (no dispatched copy)
   f.x_perm = c.act_dtype == MOE_F32 ? cv.take(tk * c.D * act_size(c)) : nullptr;
-  f.xq = is_a8(c) ? static_cast<uint8_t*>(cv.take(mxfp8_bytes(c.T, c.D))) : nullptr;
   f.H = cv.take(tk * c.F * act_size(c));
   f.y_perm = static_cast<float*>(cv.take(tk * c.D * 4));
   f.H_shared = c.shared_F > 0 ? cv.take((size_t)c.T * c.shared_F * 2) : nullptr;
@@ -165,10 +169,10 @@ moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_
 // routed row r reads row gather[r] of it). With MXFP8 activations H is
 // written as MXFP8 (codes [T*k][F], then grouped scales); the dispatched
 // x_perm is MXFP8 already (codes [T*k][D], then grouped scales), and x
-// (gathered) is first quantised into xq.
+// (gathered) is first quantised into the workspace's MXFP8 copy of x.
 hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gather,
                        const int32_t* offsets, const moe_weights& w, void* H, int32_t* tilemap,
-                       uint8_t* xq, hipStream_t s) {
+                       hipStream_t s) {
   if (c.act_dtype == MOE_F32)
     return moe::launch_ffn_f32_gate_up(c, static_cast<const float*>(x_perm), offsets,
                                        static_cast<const float*>(w.W_gate),
@@ -188,6 +192,7 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gath
   g.out = H;
   if (!is_a8(c)) return moe::launch_gemm_swiglu(g, s);
   if (gather) {
+    uint8_t* xq = xq_of(c, tilemap);
     uint8_t* xs = xq + moe::align_up((size_t)c.T * c.D, kAlign);
     e = moe::launch_quant_mxfp8(x_perm, c.T, c.D, xq, xs, true, s);
     if (e != hipSuccess) return e;
@@ -225,8 +230,8 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
 
 hipError_t run_expert_ffn(const moe_cfg& c, const void* x_perm, const int32_t* gather,
                           const int32_t* offsets, const moe_weights& w, void* H, float* y_perm,
-                          int32_t* tilemap, uint8_t* xq, hipStream_t s) {
-  hipError_t e = run_gate_up(c, x_perm, gather, offsets, w, H, tilemap, xq, s);
+                          int32_t* tilemap, hipStream_t s) {
+  hipError_t e = run_gate_up(c, x_perm, gather, offsets, w, H, tilemap, s);
   if (e != hipSuccess) return e;
   return run_down(c, H, offsets, w, y_perm, tilemap, false, s);
 }
@@ -313,7 +318,7 @@ int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int
   int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (!dev_ok(topk_idx) || !dev_ok(x) || !dev_ok(counts) || !dev_ok(offsets) ||
-      !dev_ok(slot_pos) || !dev_ok(perm_token) || !dev_ok(x_perm))
+      !dev_ok(slot_pos) || !dev_ok(perm_token) || !opt_ok(x_perm))
     return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws) || ws_bytes < dispatch_ws(*cfg)) return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
@@ -328,7 +333,7 @@ int moe_dispatch_noalloc(const moe_cfg* cfg, const int32_t* topk_idx, const void
   int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (!dev_ok(topk_idx) || !dev_ok(x) || !dev_ok(counts) || !dev_ok(offsets) ||
-      !dev_ok(slot_pos) || !dev_ok(perm_token) || !dev_ok(x_perm))
+      !dev_ok(slot_pos) || !dev_ok(perm_token) || !opt_ok(x_perm))
     return MOE_ERR_INVALID_ARG;
   if ((size_t)cfg->E * moe::num_chunks(*cfg) > moe::kDispatchScratchInts)
     return MOE_ERR_SCRATCH;
@@ -352,8 +357,7 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offset
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_expert_ffn(*cfg, x_perm, nullptr, offsets, *w, H, y_perm,
-                                   static_cast<int32_t*>(ws), nullptr,
-                                   static_cast<hipStream_t>(stream)));
+                                   static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
@@ -366,7 +370,22 @@ int moe_expert_gate_up(const moe_cfg* cfg, const void* x_perm, const int32_t* of
     return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return hip_status(run_gate_up(*cfg, x_perm, nullptr, offsets, *w, H, static_cast<int32_t*>(ws),
-                                nullptr, static_cast<hipStream_t>(stream)));
+                                static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_gate_up_gathered(const moe_cfg* cfg, const void* x, const int32_t* perm_token,
+                                const int32_t* offsets, const moe_weights* w, void* H, void* ws,
+                                size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(*cfg, w)) != MOE_OK) return st;
+  if (cfg->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!dev_ok(x) || !dev_ok(perm_token) || !dev_ok(offsets) || !dev_ok(H))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < ffn_ws(*cfg)) return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return hip_status(run_gate_up(*cfg, x, perm_token, offsets, *w, H, static_cast<int32_t*>(ws),
+                                static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_down(const moe_cfg* cfg, const void* H, const int32_t* offsets,
@@ -438,9 +457,9 @@ int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float
     e = moe::launch_dispatch(c, idx, x, cnt, off, f.slot_pos, f.perm, f.x_perm, f.chunk_ws, s);
   if (e == hipSuccess) {
     if (f.x_perm)  // fp32 activations: the VALU path reads dispatched rows
-      e = run_expert_ffn(c, f.x_perm, nullptr, off, *w, f.H, f.y_perm, f.tilemap, nullptr, s);
+      e = run_expert_ffn(c, f.x_perm, nullptr, off, *w, f.H, f.y_perm, f.tilemap, s);
     else
-      e = run_expert_ffn(c, x, f.perm, off, *w, f.H, f.y_perm, f.tilemap, f.xq, s);
+      e = run_expert_ffn(c, x, f.perm, off, *w, f.H, f.y_perm, f.tilemap, s);
   }
   if (e == hipSuccess && c.shared_F > 0) e = run_shared(c, x, *w, f.H_shared, f.y_shared, s);
   if (e == hipSuccess) e = moe::launch_combine(c, f.y_perm, f.slot_pos, tw, f.y_shared, y, s);

@@ -53,7 +53,7 @@ SYMBOLS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down",
            "moe_shared_expert", "moe_combine", "moe_forward", "moe_quantize_mxfp8",
            "moe_status_string", "moe_last_hip_error", "moe_version", "moe_set_split_wait",
-           "moe_dispatch_noalloc"]
+           "moe_dispatch_noalloc", "moe_expert_gate_up_gathered"]
 
 
 def lib():
@@ -73,6 +73,7 @@ def lib():
     L.moe_dispatch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_ffn.argtypes = [P, vp, vp, W, vp, vp, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [P, vp, vp, W, vp, vp, sz, vp]
+    L.moe_expert_gate_up_gathered.argtypes = [P, vp, vp, vp, W, vp, vp, sz, vp]
     L.moe_expert_down.argtypes = [P, vp, vp, W, vp, vp, sz, vp]
     L.moe_shared_expert.argtypes = [P, vp, W, vp, vp, vp]
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -86,7 +87,8 @@ def lib():
     L.moe_set_split_wait.argtypes = [ctypes.c_int]
     for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_dispatch_noalloc",
                  "moe_expert_ffn",
-                 "moe_expert_gate_up", "moe_expert_down", "moe_shared_expert", "moe_combine",
+                 "moe_expert_gate_up", "moe_expert_gate_up_gathered", "moe_expert_down",
+                 "moe_shared_expert", "moe_combine",
                  "moe_forward", "moe_quantize_mxfp8"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -169,17 +171,19 @@ def route(cfg: Cfg, x, W_r, bias=None, topk_idx=None, topk_w=None, logits=None,
     return topk_idx, topk_w, logits
 
 
-def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None):
+def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None, copy_rows=True):
     """moe_dispatch. x_perm is allocated in the activation dtype, [T*k, D];
     with MXFP4_A8 weights its bytes hold MXFP8 rows (codes, then grouped
-    scales; see include/moe.h)."""
+    scales; see include/moe.h). copy_rows=False passes no x_perm (the rows
+    are then gathered through perm by the gate/up GEMM)."""
     dev = x.device
     tk = cfg.T * cfg.top_k
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
     offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
     slot_pos = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
     perm = torch.full((max(tk, 1),), -1, dtype=torch.int32, device=dev)
-    x_perm = torch.empty((max(tk, 1), cfg.D), dtype=act_torch_dtype(cfg), device=dev)
+    x_perm = (torch.empty((max(tk, 1), cfg.D), dtype=act_torch_dtype(cfg), device=dev)
+              if copy_rows else None)
     if ws is None:
         ws = workspace(cfg, WS_DISPATCH, dev)
     _check(lib().moe_dispatch(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts), _p(offsets),
@@ -219,6 +223,15 @@ def expert_gate_up(cfg: Cfg, x_perm, offsets, weights: Weights, H, ws, stream=No
     w = wstruct if wstruct is not None else weights.struct()
     _check(lib().moe_expert_gate_up(ctypes.byref(cfg), _p(x_perm), _p(offsets), ctypes.byref(w),
                                     _p(H), _p(ws), ws.numel(), _stream(stream)))
+    return H
+
+
+def expert_gate_up_gathered(cfg: Cfg, x, perm, offsets, weights: Weights, H, ws, stream=None,
+                            wstruct=None):
+    w = wstruct if wstruct is not None else weights.struct()
+    _check(lib().moe_expert_gate_up_gathered(ctypes.byref(cfg), _p(x), _p(perm), _p(offsets),
+                                             ctypes.byref(w), _p(H), _p(ws), ws.numel(),
+                                             _stream(stream)))
     return H
 
 

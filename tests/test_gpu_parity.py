@@ -77,6 +77,29 @@ def test_small_fused_equals_stagewise(name):
     assert np.array_equal(b["y"], c["y"]), "two runs differ (must be deterministic)"
 
 
+@pytest.mark.parametrize("name", [n for n in SMALL if n != "tiny_fp32"])
+def test_small_gathered_gate_up_equals_dispatched(name):
+    """moe_expert_gate_up_gathered (rows read from x through perm_token, after
+    a dispatch that copies no rows) writes the same H, byte for byte, as
+    moe_expert_gate_up on the dispatched copy x_perm."""
+    cfg = SMALL[name]
+    inp = syn.make_inputs(cfg)
+    c, x, W_r, bias, w = upload.to_device(inp)
+    idx, _, _ = moe.route(c, x, W_r, bias)
+    d = moe.dispatch(c, idx, x)
+    g = moe.dispatch(c, idx, x, copy_rows=False)
+    ws = moe.workspace(c, moe.WS_EXPERT_FFN, x.device)
+    rows = cfg.T * cfg.k
+    H1 = torch.zeros((rows, cfg.F), dtype=torch.bfloat16, device=x.device)
+    H2 = torch.zeros_like(H1)
+    moe.expert_gate_up(c, d["x_perm"], d["offsets"], w, H1, ws)
+    moe.expert_gate_up_gathered(c, x, g["perm"], g["offsets"], w, H2, ws)
+    torch.cuda.synchronize()
+    for k in ("counts", "offsets", "slot_pos", "perm"):
+        assert torch.equal(d[k], g[k]), k
+    assert torch.equal(H1.view(torch.int16), H2.view(torch.int16)), "gathered gate/up differs"
+
+
 @pytest.mark.timeout(400)
 @pytest.mark.parametrize("name", syn.CONFIG_ORDER + ["fine384_mxfp4_a8"])
 def test_full_size(name):
