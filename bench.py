@@ -430,6 +430,7 @@ def main():
     # that each stage's duration is known.
     d_ws = moe.workspace(c, moe.WS_DISPATCH, dev)
     f_ws = moe.workspace(c, moe.WS_EXPERT_FFN, dev)
+    r_ws = moe.workspace(c, moe.WS_ROUTE, dev)
     tk = T * k
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
     perm = torch.empty(tk, dtype=torch.int32, device=dev)
@@ -450,9 +451,11 @@ def main():
     sp = moe._stream(stream)
 
     stages = {
-        "route": lambda: L.moe_route(P(c), x.data_ptr(), W_r.data_ptr(),
-                                     bias.data_ptr() if bias is not None else None,
-                                     idx.data_ptr(), tw.data_ptr(), None, sp),
+        # the router moe_forward runs (screened for many experts)
+        "route": lambda: L.moe_route_screened(P(c), x.data_ptr(), W_r.data_ptr(),
+                                              bias.data_ptr() if bias is not None else None,
+                                              idx.data_ptr(), tw.data_ptr(), r_ws.data_ptr(),
+                                              r_ws.numel(), sp),
         "dispatch": lambda: L.moe_dispatch(P(c), idx.data_ptr(), x.data_ptr(), counts.data_ptr(),
                                            offsets.data_ptr(), slot_pos.data_ptr(),
                                            perm.data_ptr(),

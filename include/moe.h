@@ -95,7 +95,8 @@ typedef enum {
 typedef enum {
   MOE_WS_DISPATCH = 0,
   MOE_WS_EXPERT_FFN = 1,
-  MOE_WS_FORWARD = 2
+  MOE_WS_FORWARD = 2,
+  MOE_WS_ROUTE = 3
 } moe_ws_kind;
 
 /* Layer configuration (host struct, read during the call only).
@@ -139,6 +140,7 @@ typedef struct moe_weights {
  * map and, with bf16 activations, 64 MiB of fp32 partial sums plus two
  * banks of ready flags for the GEMM tiles that are split along K, and with
  * MOE_MXFP4_A8 the MXFP8 copy of x that a gathered gate/up reads),
+ * MOE_WS_ROUTE for moe_route_screened (0 where it runs the exact router),
  * MOE_WS_FORWARD for moe_forward (all of the above plus H, y_perm, x_perm for fp32
  * activations only, the MXFP8 copy of x for MOE_MXFP4_A8 and, with a
  * shared expert, its H and output). A workspace carries state only within
@@ -157,6 +159,24 @@ int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes);
  *   logits [T][E] fp32 is an optional output (NULL: not written). */
 int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
               int32_t* topk_idx, float* topk_w, float* logits, void* stream);
+
+/* moe_route without the logits output, for many experts: the same
+ * topk_idx and topk_w, bit for bit, with most of the fp32 chains skipped.
+ * An estimate of every logit on the bf16 MFMA (x times bf16(W_r)) with a
+ * rigorous bound eps_t on its distance from the defined fp32 chain (from
+ * ||x_t||, the norms of W_r's columns and of their bf16 residuals, and the
+ * fp32 accumulation error bound D u / (1 - D u) of the chain and, with a
+ * safety factor, of the MFMA) keeps, per token, the experts whose estimated
+ * key is within 2 eps_t of the k-th largest: the exact top k is always
+ * among them ("ops-transformer" pitfall 3: the router is FP32; its
+ * performance comparison counts routing among the overheads). Only their
+ * exact chains run; selection and weights then use the exact router's
+ * code. Used with bf16 activations, E >= 256 and any gating except softmax
+ * without renormalisation; otherwise this call runs the exact router
+ * (workspace size 0). Workspace: MOE_WS_ROUTE. moe_forward takes this path
+ * whenever it applies. */
+int moe_route_screened(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch ("moe f&b compute flow" Dispatch; "ops-transformer" MoEForward
  * step 3 GetTokensForExpert/Gather, pitfall 1). Groups the (t, j) pairs by

@@ -18,7 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "router.hip", "dispatch.hip", "ffn_f32.hip", "gemm16.hip", "gemm_a8.hip", "combine.hip"]
+SOURCES = ["api.hip", "router.hip", "route_fast.hip", "dispatch.hip", "ffn_f32.hip", "gemm16.hip",
+           "gemm_a8.hip", "combine.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops stay off (plain v_fma_f32 / v_add_f32 only)

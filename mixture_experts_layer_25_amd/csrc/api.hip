@@ -120,7 +120,12 @@ uint8_t* xq_of(const moe_cfg& c, int32_t* tilemap) {
   return reinterpret_cast<uint8_t*>(tilemap) + tilemap_bytes(c) + moe::split_bytes(c);
 }
 
+size_t route_ws(const moe_cfg& c) {
+  return moe::router_screen_applies(c) ? moe::router_screen_ws_bytes(c) : 0;
+}
+
 struct ForwardWs {
+  void* route;  // screened router's workspace (when it applies)
   int32_t *idx, *counts, *offsets, *slot_pos, *perm, *chunk_ws, *tilemap;
   float *w, *y_perm, *y_shared;
   void *x_perm, *H, *H_shared;
@@ -138,6 +143,7 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   f.slot_pos = static_cast<int32_t*>(cv.take(tk * 4));
   f.perm = static_cast<int32_t*>(cv.take(tk * 4));
   f.chunk_ws = static_cast<int32_t*>(cv.take(dispatch_ws(c)));
+  f.route = route_ws(c) ? cv.take(route_ws(c)) : nullptr;
   f.tilemap = static_cast<int32_t*>(cv.take(ffn_ws(c)));
   // bf16: gate/up gathers its rows from x through perm (no dispatched copy)
   f.x_perm = c.act_dtype == MOE_F32 ? cv.take(tk * c.D * act_size(c)) : nullptr;
@@ -296,6 +302,7 @@ int moe_workspace_size(const moe_cfg* cfg, int kind, size_t* bytes) {
     case MOE_WS_DISPATCH: *bytes = dispatch_ws(*cfg); return MOE_OK;
     case MOE_WS_EXPERT_FFN: *bytes = cfg->act_dtype == MOE_F32 ? 0 : ffn_ws(*cfg); return MOE_OK;
     case MOE_WS_FORWARD: *bytes = carve_forward(*cfg, nullptr).bytes; return MOE_OK;
+    case MOE_WS_ROUTE: *bytes = route_ws(*cfg); return MOE_OK;
     default: return MOE_ERR_INVALID_ARG;
   }
 }
@@ -310,6 +317,20 @@ int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* 
   if (cfg->T == 0) return MOE_OK;
   return hip_status(moe::launch_router(*cfg, x, W_r, bias, topk_idx, topk_w, logits,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_route_screened(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!dev_ok(x) || !dev_ok(W_r) || !dev_ok(topk_idx) || !dev_ok(topk_w) || !opt_ok(bias))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = route_ws(*cfg);
+  if (need && (!ws || !aligned16(ws) || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!need) return hip_status(moe::launch_router(*cfg, x, W_r, bias, topk_idx, topk_w, nullptr, s));
+  return hip_status(moe::launch_router_screened(*cfg, x, W_r, bias, topk_idx, topk_w, ws, s));
 }
 
 int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -452,7 +473,8 @@ int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float
   float* tw = topk_w ? topk_w : f.w;
   int32_t* cnt = counts ? counts : f.counts;
   int32_t* off = offsets ? offsets : f.offsets;
-  hipError_t e = moe::launch_router(c, x, W_r, bias, idx, tw, nullptr, s);
+  hipError_t e = f.route ? moe::launch_router_screened(c, x, W_r, bias, idx, tw, f.route, s)
+                         : moe::launch_router(c, x, W_r, bias, idx, tw, nullptr, s);
   if (e == hipSuccess)
     e = moe::launch_dispatch(c, idx, x, cnt, off, f.slot_pos, f.perm, f.x_perm, f.chunk_ws, s);
   if (e == hipSuccess) {

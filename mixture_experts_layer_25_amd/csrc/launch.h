@@ -49,6 +49,20 @@ constexpr size_t kDispatchScratchInts = 1 << 18;
 // first call on each device).
 hipError_t dispatch_scratch(int32_t** out);
 
+// Screened router (route_fast.hip): MFMA estimates of the logits with a
+// rigorous error bound pick each token's candidate experts, and only their
+// exact fp32 chains are run; the indices and weights equal the exact
+// router's. Applies with bf16 activations, at least kScreenMinE experts and
+// any gating except softmax without renormalisation (whose weights need
+// every expert's exact logit). Below 256 experts (measured: 128) the exact
+// router is as fast, so the screen starts there.
+constexpr int kScreenMinE = 256;
+bool router_screen_applies(const moe_cfg& c);
+size_t router_screen_ws_bytes(const moe_cfg& c);
+hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* W_r,
+                                  const float* bias, int32_t* idx, float* w, void* ws,
+                                  hipStream_t s);
+
 // chunk_ws: int32 [E][num_chunks]
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,

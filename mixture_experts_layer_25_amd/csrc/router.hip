@@ -22,6 +22,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "gating.h"
 #include "launch.h"
 
 namespace moe {
@@ -62,14 +63,15 @@ __device__ __forceinline__ void select_topk(const RouterArgs& a, const float* lg
       key[j] = avail[j] ? lgt[j] + (a.bias ? a.bias[e] : 0.0f) : -INFINITY;
       if (a.logits && t < a.T && avail[j]) a.logits[(size_t)t * a.E + e] = lgt[j];
     }
-    // softmax normaliser over all experts: max key, then sum of exp(key - max)
+    // largest key, and (softmax without renormalisation) the normaliser over
+    // all experts, the sum of exp(key - max)
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < RE; ++j) m = fmaxf(m, key[j]);
 #pragma unroll
     for (int o = NE / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, NE));
     float Z = 0.0f;
-    if (a.gating == MOE_GATE_SOFTMAX) {
+    if (a.gating == MOE_GATE_SOFTMAX && !a.renorm) {
 #pragma unroll
       for (int j = 0; j < RE; ++j)
         if (avail[j]) Z += expf(key[j] - m);
@@ -108,15 +110,7 @@ __device__ __forceinline__ void select_topk(const RouterArgs& a, const float* lg
 #pragma unroll
         for (int j = 0; j < RE; ++j)
           if (te + NE * j == bi) avail[j] = false;
-        float wv;
-        if (a.gating == MOE_GATE_SOFTMAX) {
-          wv = expf(bk - m) / Z;
-        } else if (a.gating == MOE_GATE_SIGMOID) {
-          wv = 1.0f / (1.0f + expf(-bl));
-        } else {
-          const float sp = fmaxf(bl, 0.0f) + log1pf(expf(-fabsf(bl)));
-          wv = sqrtf(sp);
-        }
+        const float wv = gate_weight(a.gating, a.renorm, bk, bl, m, Z);
         wsel[s] = wv;
         isel[s] = bi;
         wsum += wv;

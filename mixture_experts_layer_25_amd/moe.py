@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 F32, BF16, MXFP4, MXFP4_A8 = 0, 1, 2, 3
 GATE_SOFTMAX, GATE_SIGMOID, GATE_SQRT_SOFTPLUS = 0, 1, 2
-WS_DISPATCH, WS_EXPERT_FFN, WS_FORWARD = 0, 1, 2
+WS_DISPATCH, WS_EXPERT_FFN, WS_FORWARD, WS_ROUTE = 0, 1, 2, 3
 
 _GATING = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID, "sqrt_softplus": GATE_SQRT_SOFTPLUS}
 _DT = {"f32": F32, "fp32": F32, "bf16": BF16, "mxfp4": MXFP4, "mxfp4_a8": MXFP4_A8}
@@ -53,7 +53,8 @@ SYMBOLS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down",
            "moe_shared_expert", "moe_combine", "moe_forward", "moe_quantize_mxfp8",
            "moe_status_string", "moe_last_hip_error", "moe_version", "moe_set_split_wait",
-           "moe_dispatch_noalloc", "moe_expert_gate_up_gathered"]
+           "moe_dispatch_noalloc", "moe_expert_gate_up_gathered",
+           "moe_route_screened"]
 
 
 def lib():
@@ -69,6 +70,7 @@ def lib():
     W = ctypes.POINTER(_Weights)
     L.moe_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route_screened.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_ffn.argtypes = [P, vp, vp, W, vp, vp, vp, sz, vp]
@@ -85,7 +87,8 @@ def lib():
     L.moe_version.restype = ctypes.c_int
     L.moe_set_split_wait.restype = ctypes.c_int
     L.moe_set_split_wait.argtypes = [ctypes.c_int]
-    for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_dispatch_noalloc",
+    for name in ("moe_workspace_size", "moe_route", "moe_route_screened", "moe_dispatch",
+                 "moe_dispatch_noalloc",
                  "moe_expert_ffn",
                  "moe_expert_gate_up", "moe_expert_gate_up_gathered", "moe_expert_down",
                  "moe_shared_expert", "moe_combine",
@@ -169,6 +172,22 @@ def route(cfg: Cfg, x, W_r, bias=None, topk_idx=None, topk_w=None, logits=None,
     _check(lib().moe_route(ctypes.byref(cfg), _p(x), _p(W_r), _p(bias), _p(topk_idx),
                            _p(topk_w), _p(logits), _stream(stream)))
     return topk_idx, topk_w, logits
+
+
+def route_screened(cfg: Cfg, x, W_r, bias=None, topk_idx=None, topk_w=None, ws=None,
+                   stream=None):
+    """moe_route_screened: the same indices and weights as route(), with the
+    MFMA screen and exact chains for the candidate experts only."""
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(cfg, WS_ROUTE, dev)
+    _check(lib().moe_route_screened(ctypes.byref(cfg), _p(x), _p(W_r), _p(bias), _p(topk_idx),
+                                    _p(topk_w), _p(ws), ws.numel(), _stream(stream)))
+    return topk_idx, topk_w
 
 
 def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None, copy_rows=True):

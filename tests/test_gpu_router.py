@@ -57,3 +57,68 @@ def test_router_instance(E, k, D, gating, renorm, act):
     torch.cuda.synchronize()
     assert np.array_equal(gi2.cpu().numpy(), idx)
     assert np.array_equal(gw2.cpu().numpy().view(np.uint32), gw.view(np.uint32))
+
+
+SCREEN_CASES = [
+    # (E, k, D, gating, renorm); the screen runs from 256 experts, below
+    # that the entry point runs the exact router
+    (128, 8, 1024, syn.GATE_SOFTMAX, 1),
+    (256, 8, 512, syn.GATE_SIGMOID, 1),
+    (256, 16, 256, syn.GATE_SIGMOID, 0),
+    (300, 9, 512, syn.GATE_SQRT_SOFTPLUS, 0),
+    (384, 6, 1024, syn.GATE_SQRT_SOFTPLUS, 0),
+    (512, 16, 256, syn.GATE_SOFTMAX, 1),
+    (1024, 6, 512, syn.GATE_SQRT_SOFTPLUS, 0),
+    (260, 5, 4096, syn.GATE_SOFTMAX, 1),
+    # softmax without renormalisation: the screened entry runs the exact router
+    (384, 4, 256, syn.GATE_SOFTMAX, 0),
+]
+
+
+def _route_both(cfg, inp):
+    c = upload.cfg_of(cfg)
+    x = upload._dev_bits(inp.x, "cuda")
+    W_r = upload._dev_bits(inp.W_r, "cuda")
+    bias = upload._dev_bits(inp.bias, "cuda") if inp.bias is not None else None
+    ei, ew, _ = moe.route(c, x, W_r, bias)
+    si, sw = moe.route_screened(c, x, W_r, bias)
+    torch.cuda.synchronize()
+    return ei.cpu().numpy(), ew.cpu().numpy(), si.cpu().numpy(), sw.cpu().numpy()
+
+
+@pytest.mark.parametrize("E,k,D,gating,renorm", SCREEN_CASES)
+def test_screened_router_equals_exact(E, k, D, gating, renorm):
+    """moe_route_screened (MFMA estimate, candidates within the error bound,
+    exact chains for those only) writes the same indices and the same weight
+    bits as the exact router, and the indices equal the oracle's."""
+    cfg = syn.Config(f"screen_E{E}", T=777, D=D, E=E, k=k, F=64, gating=gating, renorm=renorm,
+                     bias="normal", bias_sigma=0.3)
+    print(f"[router] screened {cfg}", flush=True)
+    inp = syn.make_inputs(cfg, with_experts=False)
+    ei, ew, si, sw = _route_both(cfg, inp)
+    _, idx, w = oracle.route(cfg, inp.x, inp.W_r, inp.bias)
+    assert np.array_equal(si, idx), "screened indices differ from the oracle"
+    assert np.array_equal(si, ei)
+    assert np.array_equal(sw.view(np.uint32), ew.view(np.uint32)), "weights not bit-identical"
+
+
+def test_screened_router_ties_and_zero_rows():
+    """All-tie tokens (zero rows without a bias: every expert is a candidate,
+    several passes of exact chains), duplicated W_r columns (exact ties,
+    decided toward the lower index) and scaled rows."""
+    E, k, D, T = 320, 6, 512, 300
+    cfg = syn.Config("screen_ties", T=T, D=D, E=E, k=k, F=64, gating=syn.GATE_SQRT_SOFTPLUS,
+                     renorm=0)
+    inp = syn.make_inputs(cfg, with_experts=False)
+    x = syn.bf16_bits_to_f32(inp.x).copy()
+    x[::7] = 0.0                     # zero rows
+    x[3::11] *= 40.0                 # large rows
+    inp.x = syn.f32_to_bf16_bits(x)
+    inp.W_r[:, 50] = inp.W_r[:, 10]  # duplicated experts
+    inp.W_r[:, 151] = inp.W_r[:, 150]
+    ei, ew, si, sw = _route_both(cfg, inp)
+    _, idx, w = oracle.route(cfg, inp.x, inp.W_r, inp.bias)
+    assert np.array_equal(si, idx)
+    assert np.array_equal(si, ei)
+    assert np.array_equal(sw.view(np.uint32), ew.view(np.uint32))
+    assert (idx[::7] == np.arange(k)).all()   # zero rows: the lowest indices
