@@ -52,7 +52,8 @@ typedef __bf16 bf16v8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMaxK = 16;
 constexpr int kScrTM = 64;    // screen tile: tokens (experts: 64 or 128)
-constexpr int kExTB = 128;    // exact chains: tokens per workgroup
+constexpr int kExTB = 256;    // exact chains: tokens per workgroup
+constexpr int kExER = 96;     // exact chains: experts per workgroup
 constexpr int kExDK = 64;     // exact chains: d per staged chunk
 
 struct ScreenWs {
@@ -89,9 +90,8 @@ ScreenWs carve(const moe_cfg& c, void* base) {
   w.ncand = reinterpret_cast<int32_t*>(take((size_t)c.T * 4));
   w.exl = reinterpret_cast<float*>(take(TE * 4));
   w.exk = reinterpret_cast<float*>(take(TE * 4));
-  const int erx = 64;  // experts per exact-chain workgroup
   w.gpairs = reinterpret_cast<int32_t*>(
-      take((size_t)ceil_div(c.T, kExTB) * kExTB * ceil_div(c.E, erx) * erx * 4));
+      take((size_t)ceil_div(c.T, kExTB) * kExTB * ceil_div(c.E, kExER) * kExER * 4));
   w.bytes = align_up(off, 256);
   return w;
 }
@@ -168,7 +168,9 @@ __global__ __launch_bounds__(256) void screen_norms_kernel(const float* __restri
 // ---- 2. screen: S = x . bf16(W_r) on v_mfma_f32_16x16x32_bf16. Tile 64
 // tokens x TN = 128 experts, 4 waves, wave w owns experts (TN/4) w .. of
 // the tile (4 x TN/64 MFMA tiles). Operands staged in LDS per 32-k step (A rows and
-// W^T rows, 64 bytes each, read as 16-byte fragments), double-buffered
+// W^T rows, 64 bytes each, read as 16-byte fragments; k-group g of row r at
+// slot g ^ ((r >> 2) & 3), so that the 16 lanes of a read pass, rows r..r+15
+// of one k-group, hit 16 distinct 16-byte bank groups), double-buffered
 // through registers. Lane l supplies row l%16 of A and column l%16 of B with
 // k = 8 (l/16) .. +7 and holds rows 4 (l/16) + r of column l%16 of the 16 x
 // 16 result. The workgroups of the first expert tile also sum x_t^2 in
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kScrTM, e0 = blockIdx.y * TN;
   const int ar = tid >> 2, ak = tid & 3;
+  const int aslot = 8 * (ak ^ ((ar >> 2) & 3));
   const uint16_t* ag = x + (size_t)min(t0 + ar, T - 1) * D + 8 * ak;
   const uint16_t* bg0 = whi + (size_t)min(e0 + ar, E - 1) * D + 8 * ak;
   const uint16_t* bg1 = whi + (size_t)min(e0 + 64 + ar, E - 1) * D + 8 * ak;
@@ -198,9 +201,9 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
     if (TN == 128) rb1 = *reinterpret_cast<const uint4*>(bg1 + kt * 32);
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(&As[buf][ar][8 * ak]) = ra;
-    *reinterpret_cast<uint4*>(&Bs[buf][ar][8 * ak]) = rb0;
-    if (TN == 128) *reinterpret_cast<uint4*>(&Bs[buf][64 + ar][8 * ak]) = rb1;
+    *reinterpret_cast<uint4*>(&As[buf][ar][aslot]) = ra;
+    *reinterpret_cast<uint4*>(&Bs[buf][ar][aslot]) = rb0;
+    if (TN == 128) *reinterpret_cast<uint4*>(&Bs[buf][64 + ar][aslot]) = rb1;
     if (norm) {
       const uint32_t v[4] = {ra.x, ra.y, ra.z, ra.w};
 #pragma unroll
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int l16 = lane & 15, g = lane >> 4;
+  const int rslot = 8 * (g ^ ((l16 >> 2) & 3));  // rows 16 i + l16 share bits 2-3 of l16
   const int nk = D / 32;
   load(0);
   store(0);
@@ -226,10 +230,10 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
     if (kt + 1 < nk) load(kt + 1);
     bf16v8_t a[4], b[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16v8_t*>(&As[buf][16 * i + l16][8 * g]);
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16v8_t*>(&As[buf][16 * i + l16][rslot]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      b[j] = *reinterpret_cast<const bf16v8_t*>(&Bs[buf][(TN / 4) * wave + 16 * j + l16][8 * g]);
+      b[j] = *reinterpret_cast<const bf16v8_t*>(&Bs[buf][(TN / 4) * wave + 16 * j + l16][rslot]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -330,8 +334,9 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
   if (lane == 0) ncand[t] = base;
 }
 
-// ---- 4. exact chains of the candidates. Workgroup = 128 tokens x ERX
-// experts. The block's candidate pairs are counted per expert and listed by
+// ---- 4. exact chains of the candidates. Workgroup = 256 tokens x ERX = 96
+// experts (384 experts: 4 x 64 = 256 workgroups; a tile this large lets
+// each staged row serve several pairs). The block's candidate pairs are counted per expert and listed by
 // expert (in the workspace); a unit is one expert and up to 4 of its
 // candidate tokens, so a thread runs 4 independent chains that read the
 // expert's weights once per 4 d. The x rows of the block and the W_r^T rows
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
 // pair's slot in its token's candidate list. More units than threads:
 // further passes over d.
 template <int ERX>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void screen_exact_kernel(
+__global__ __launch_bounds__(512) void screen_exact_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wt, const float* __restrict__ bias,
     const int16_t* __restrict__ cand, const int32_t* __restrict__ ncand, int T, int D, int E,
     int32_t* __restrict__ gpairs, float* __restrict__ exl, float* __restrict__ exk) {
@@ -351,7 +356,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   constexpr int NXV = TB * DK / 8 / NTH;    // 16-byte x pieces per thread per chunk
   constexpr int NWV = ERX * DK / 4 / NTH;   // 16-byte W pieces per thread per chunk
   static_assert(NXV * NTH * 8 == TB * DK && NWV * NTH * 4 == ERX * DK, "chunk shape");
-  static_assert(ERX <= 64, "one wave scans the expert counts");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TB][XP];
   __shared__ __attribute__((aligned(16))) float ws[2][ERX][WP];
   __shared__ int cnt[ERX], seg[ERX + 1], ucum[ERX + 1];
@@ -372,20 +376,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if (e >= e0) atomicAdd(&cnt[e - e0], 1);
   }
   __syncthreads();
-  if (tid < 64) {
-    const int v = tid < ERX ? cnt[tid] : 0;
-    const int incl = wave_inclusive_scan(v);
-    const int nu = (v + UT - 1) / UT;
-    const int uincl = wave_inclusive_scan(nu);
-    if (tid < ERX) {
-      seg[tid] = incl - v;
-      ucum[tid] = uincl - nu;
-      cnt[tid] = incl - v;  // the expert's cursor
+  if (tid == 0) {
+    int a = 0, b = 0;
+    for (int e = 0; e < ERX; ++e) {
+      const int v = cnt[e];
+      seg[e] = a;
+      ucum[e] = b;
+      cnt[e] = a;  // the expert's cursor
+      a += v;
+      b += (v + UT - 1) / UT;
     }
-    if (tid == 63) {
-      seg[ERX] = incl;
-      ucum[ERX] = uincl;
-    }
+    seg[ERX] = a;
+    ucum[ERX] = b;
   }
   __syncthreads();
   for (int i = 0; i < nc; ++i) {
@@ -596,7 +598,7 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   else if (nj <= 6) screen_cand_kernel<6><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
   else if (nj <= 8) screen_cand_kernel<8><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
   else screen_cand_kernel<16><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
-  screen_exact_kernel<64><<<dim3(ceil_div(T, kExTB), ceil_div(E, 64)), 512, 0, s>>>(
+  screen_exact_kernel<kExER><<<dim3(ceil_div(T, kExTB), ceil_div(E, kExER)), 512, 0, s>>>(
       xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
   screen_select_kernel<1><<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
                                               c.gating, c.renorm, idx, w);
