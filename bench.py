@@ -186,23 +186,47 @@ def summarize_trace(run_dir, workload, command):
     print(out)
 
 
+# MFMA flops per busy pipe cycle and SIMD: v_mfma_f32_16x16x32_bf16 (16384
+# flops in 16 cycles) and the block-scaled fp8 x fp4 MFMA (twice the rate)
+MFMA_FLOP_PER_CYCLE = {"gemm16": 1024, "gemm_a8": 2048}
+XCDS = 8
+
+
 def summarize_mfma(run_dir, workload, command):
-    """rocprofv3 --pmc MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE
-    times the SIMD count, in per cent) -> profiles/mfma_util_<workload>.txt,
-    the mean per kernel over its dispatches."""
+    """rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE -> profiles/mfma_util_<workload>.txt:
+    per kernel the mean over its dispatches of MfmaUtil
+    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), per cent), of the
+    clock under load (GRBM_GUI_ACTIVE cycles, which the counter reports
+    summed over the 8 XCDs, over the dispatch's duration; meaningless for
+    dispatches of a few microseconds)
+    and of the rate they imply for an MFMA kernel, MfmaUtil x SIMDs x flops
+    per busy cycle x clock (1024 SIMDs on MI355X)."""
     from collections import defaultdict
-    per = defaultdict(list)
+    util, clk, dur = defaultdict(list), defaultdict(list), defaultdict(list)
     for r in read_csv(find_one(run_dir, "counter_collection.csv")):
+        k = short_name(r["Kernel_Name"])
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         if r["Counter_Name"] == "MfmaUtil":
-            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+            util[k].append(float(r["Counter_Value"]))
+            dur[k].append(ns / 1e3)
+        elif r["Counter_Name"] == "GRBM_GUI_ACTIVE" and ns > 0:
+            # the counter comes summed over the XCDs (8 on MI355X)
+            clk[k].append(float(r["Counter_Value"]) / XCDS / ns)
     out = os.path.join(ROOT, "profiles", f"mfma_util_{workload}.txt")
-    lines = [f"# MFMA pipe utilisation per dispatch (rocprofv3 derived counter MfmaUtil = "
-             f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), per cent), workload {workload}",
+    lines = [f"# MFMA pipe utilisation (MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
+             f"SIMDs), per cent), clock under load (GRBM_GUI_ACTIVE / dispatch duration) and the "
+             f"MFMA rate they imply (MfmaUtil x 1024 SIMDs x flop per busy cycle x clock), "
+             f"workload {workload}",
              f"# command: {command}",
-             f"{'kernel':90s} {'dispatches':>10s} {'MfmaUtil_%':>10s}"]
-    for k in sorted(per, key=lambda k: -sum(per[k]) / len(per[k])):
-        v = per[k]
-        lines.append(f"{k:90s} {len(v):10d} {sum(v) / len(v):10.1f}")
+             f"{'kernel':90s} {'dispatches':>10s} {'MfmaUtil_%':>10s} {'clock_GHz':>9s} "
+             f"{'avg_us':>9s} {'implied_TF':>10s}"]
+    for k in sorted(util, key=lambda k: -sum(util[k]) / len(util[k])):
+        u = sum(util[k]) / len(util[k])
+        c = sum(clk[k]) / len(clk[k]) if clk.get(k) else float("nan")
+        fpc = next((v for n, v in MFMA_FLOP_PER_CYCLE.items() if k.startswith(n)), 0)
+        tf = u / 100 * 1024 * fpc * c * 1e9 / 1e12 if fpc else float("nan")
+        lines.append(f"{k:90s} {len(util[k]):10d} {u:10.1f} {c:9.3f} "
+                     f"{sum(dur[k]) / len(dur[k]):9.1f} {tf:10.1f}")
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
 
