@@ -7,10 +7,11 @@
 // weight * expert output; "DeepSeek-V4.1-Flash fine-grained MoE (5A)"
 // sec. 3: the shared expert's output is added once.
 //
-// One wave per token. Each lane owns 8 consecutive columns: it gathers the
-// token's kept y_perm rows (fp32, 2 x 16-byte loads per row), accumulates
-// slot by slot in ascending order with fused multiply-adds, adds the shared
-// expert row, and stores 8 outputs at once. HBM-bound.
+// One wave per token. Each lane owns groups of 8 consecutive columns (four
+// groups in flight per iteration): it gathers the token's kept y_perm rows
+// (fp32, 2 x 16-byte loads per row and group), accumulates slot by slot in
+// ascending order with fused multiply-adds, adds the shared expert row, and
+// stores 8 outputs at once. HBM-bound.
 #include "common.h"
 #include "launch.h"
 
@@ -35,43 +36,67 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
     w[j] = j < k ? topk_w[(size_t)t * k + j] : 0.0f;
   }
+  // four groups of 8 columns per iteration (v, v + 64, v + 128, v + 192):
+  // all their loads are in flight together; each column's sum keeps the
+  // order slot 0, 1, ..., then the shared row
+  constexpr int UN = 4;
   const int nv = D / 8;
-  for (int v = lane; v < nv; v += 64) {
-    float acc[8];
+  for (int v0 = lane; v0 < nv; v0 += 64 * UN) {
+    float acc[UN][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int u = 0; u < UN; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (pos[j] >= 0) {
-        const float4* src = reinterpret_cast<const float4*>(y_perm + (size_t)pos[j] * D) + 2 * v;
-        const float4 a = src[0], b = src[1];
-        acc[0] = __builtin_fmaf(w[j], a.x, acc[0]);
-        acc[1] = __builtin_fmaf(w[j], a.y, acc[1]);
-        acc[2] = __builtin_fmaf(w[j], a.z, acc[2]);
-        acc[3] = __builtin_fmaf(w[j], a.w, acc[3]);
-        acc[4] = __builtin_fmaf(w[j], b.x, acc[4]);
-        acc[5] = __builtin_fmaf(w[j], b.y, acc[5]);
-        acc[6] = __builtin_fmaf(w[j], b.z, acc[6]);
-        acc[7] = __builtin_fmaf(w[j], b.w, acc[7]);
+        const float4* src = reinterpret_cast<const float4*>(y_perm + (size_t)pos[j] * D);
+        float4 a[UN], b[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const int v = v0 + 64 * u;
+          if (v < nv) {
+            a[u] = src[2 * v];
+            b[u] = src[2 * v + 1];
+          } else {
+            a[u] = b[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          acc[u][0] = __builtin_fmaf(w[j], a[u].x, acc[u][0]);
+          acc[u][1] = __builtin_fmaf(w[j], a[u].y, acc[u][1]);
+          acc[u][2] = __builtin_fmaf(w[j], a[u].z, acc[u][2]);
+          acc[u][3] = __builtin_fmaf(w[j], a[u].w, acc[u][3]);
+          acc[u][4] = __builtin_fmaf(w[j], b[u].x, acc[u][4]);
+          acc[u][5] = __builtin_fmaf(w[j], b[u].y, acc[u][5]);
+          acc[u][6] = __builtin_fmaf(w[j], b[u].z, acc[u][6]);
+          acc[u][7] = __builtin_fmaf(w[j], b[u].w, acc[u][7]);
+        }
       }
     }
-    if (y_shared) {
-      const float4* src = reinterpret_cast<const float4*>(y_shared + (size_t)t * D) + 2 * v;
-      const float4 a = src[0], b = src[1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-    }
-    if (OUT_BF16) {
-      uint4 o;
-      o.x = pack_bf16x2(acc[0], acc[1]);
-      o.y = pack_bf16x2(acc[2], acc[3]);
-      o.z = pack_bf16x2(acc[4], acc[5]);
-      o.w = pack_bf16x2(acc[6], acc[7]);
-      reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (size_t)t * D)[v] = o;
-    } else {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * D) + 2 * v;
-      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int v = v0 + 64 * u;
+      if (v >= nv) continue;
+      if (y_shared) {
+        const float4* src = reinterpret_cast<const float4*>(y_shared + (size_t)t * D) + 2 * v;
+        const float4 a = src[0], b = src[1];
+        acc[u][0] += a.x; acc[u][1] += a.y; acc[u][2] += a.z; acc[u][3] += a.w;
+        acc[u][4] += b.x; acc[u][5] += b.y; acc[u][6] += b.z; acc[u][7] += b.w;
+      }
+      if (OUT_BF16) {
+        uint4 o;
+        o.x = pack_bf16x2(acc[u][0], acc[u][1]);
+        o.y = pack_bf16x2(acc[u][2], acc[u][3]);
+        o.z = pack_bf16x2(acc[u][4], acc[u][5]);
+        o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+        reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (size_t)t * D)[v] = o;
+      } else {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * D) + 2 * v;
+        dst[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+        dst[1] = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+      }
     }
   }
 }
