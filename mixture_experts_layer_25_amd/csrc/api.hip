@@ -155,6 +155,10 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   return f;
 }
 
+// MXFP4 weights with bf16 activations run an expert's last M-tile of at
+// most 128 rows as a wide tile (gemm16_mx_kernel); the other GEMMs do not.
+bool wide_tiles(const moe_cfg& c) { return is_mx(c) && !is_a8(c); }
+
 moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap) {
   moe::GemmProblem g{};
   g.tilemap = tilemap;
@@ -183,7 +187,7 @@ hipError_t run_gate_up(const moe_cfg& c, const void* x_perm, const int32_t* gath
     return moe::launch_ffn_f32_gate_up(c, static_cast<const float*>(x_perm), offsets,
                                        static_cast<const float*>(w.W_gate),
                                        static_cast<const float*>(w.W_up), static_cast<float*>(H), s);
-  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, split_flags_of(c, tilemap), s);
+  hipError_t e = moe::launch_tilemap(c, offsets, tilemap, split_flags_of(c, tilemap), wide_tiles(c), s);
   if (e != hipSuccess) return e;
   moe::GemmProblem g = routed_problem(c, offsets, tilemap);
   g.A = x_perm;
@@ -218,7 +222,7 @@ hipError_t run_down(const moe_cfg& c, const void* H, const int32_t* offsets, con
     return moe::launch_ffn_f32_down(c, static_cast<const float*>(H), offsets,
                                     static_cast<const float*>(w.W_down), y_perm, s);
   if (rebuild_map) {
-    hipError_t e = moe::launch_tilemap(c, offsets, tilemap, split_flags_of(c, tilemap), s);
+    hipError_t e = moe::launch_tilemap(c, offsets, tilemap, split_flags_of(c, tilemap), wide_tiles(c), s);
     if (e != hipSuccess) return e;
   }
   moe::GemmProblem g = routed_problem(c, offsets, tilemap);

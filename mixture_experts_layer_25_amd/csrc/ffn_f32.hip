@@ -3,8 +3,10 @@
 // "ops-transformer MoE operator on Ascend NPU", optimisation 3: all experts'
 // matmuls in one launch although each expert has a different number of
 // rows. The tile map lists every (expert, first row) M-tile of BM rows over
-// the kept segments; the GEMM grid is sized on the host for the worst case
-// and surplus workgroups exit, so no count travels back to the host.
+// the kept segments (an expert's last M-tile of at most BM/2 rows, when
+// wide tiles are on, in a second list); the GEMM grid is sized on the host
+// for the worst case and surplus workgroups exit, so no count travels back
+// to the host.
 //
 // The fp32 path ("FFN, SwiGLU and MoE" sec. 2: H = SiLU(x W_gate) * (x W_up),
 // y = H W_down) is for fp32 activations and weights; it runs one workgroup
@@ -17,9 +19,12 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int bm, int32_t* __restrict__ tilemap,
+                                                       int bm, int wide_rows,
+                                                       int32_t* __restrict__ tilemap,
                                                        int32_t* __restrict__ flags) {
-  __shared__ int wave_tot[16];
+  // wide_rows > 0: an expert's last M-tile with at most wide_rows rows is a
+  // wide tile, listed after all regular M-tiles
+  __shared__ int wave_tot[2][16];
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6;
   int rows = 0, start = 0;
@@ -27,17 +32,36 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
     start = offsets[e];
     rows = offsets[e + 1] - start;
   }
-  const int nt = (rows + bm - 1) / bm;
+  const int full = rows / bm, rem = rows - full * bm;
+  const int nw = (wide_rows > 0 && rem > 0 && rem <= wide_rows) ? 1 : 0;
+  const int nt = full + (rem > 0 ? 1 : 0) - nw;  // regular M-tiles
   const int incl = wave_inclusive_scan(nt);
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int base = incl - nt;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  for (int i = 0; i < nt; ++i) {
-    tilemap[1 + 2 * (base + i)] = e;
-    tilemap[2 + 2 * (base + i)] = start + i * bm;
+  const int inclw = wave_inclusive_scan(nw);
+  if (lane == 63) {
+    wave_tot[0][wave] = incl;
+    wave_tot[1][wave] = inclw;
   }
-  if (e == 1023) tilemap[0] = base + nt;
+  __syncthreads();
+  int base = incl - nt, basew = inclw - nw, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) {
+      base += wave_tot[0][w];
+      basew += wave_tot[1][w];
+    }
+    total += wave_tot[0][w];
+  }
+  for (int i = 0; i < nt; ++i) {
+    tilemap[2 + 2 * (base + i)] = e;
+    tilemap[3 + 2 * (base + i)] = start + i * bm;
+  }
+  if (nw) {
+    tilemap[2 + 2 * (total + basew)] = e;
+    tilemap[3 + 2 * (total + basew)] = start + full * bm;
+  }
+  if (e == 1023) {
+    tilemap[0] = total;
+    tilemap[1] = wide_rows > 0 ? basew + nw : -1;
+  }
   if (flags && e < 2 * kSplitSlots) flags[e] = 0;  // both banks
 }
 
@@ -100,8 +124,8 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
-                          int32_t* flags, hipStream_t s) {
-  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, kBM, tilemap, flags);
+                          int32_t* flags, bool wide, hipStream_t s) {
+  tilemap_kernel<<<1, 1024, 0, s>>>(offsets, c.E, kBM, wide ? kBM / 2 : 0, tilemap, flags);
   return hipGetLastError();
 }
 

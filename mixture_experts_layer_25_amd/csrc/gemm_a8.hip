@@ -505,6 +505,7 @@ hipError_t launch_gemm_a8(const GemmProblem& p, bool swiglu, hipStream_t s) {
   a.K = p.K;
   a.N = p.N;
   a.n_tiles_n = swiglu ? ceil_div(p.N, 128) : ceil_div(p.N, 256);
+  a.n_tiles_w = 1;  // no wide tiles: the tile map is built without them
   a.split_ws = p.split_ws;
   a.split_flags = p.split_flags;
   a.split_wait = p.split_wait;

@@ -2,7 +2,10 @@
 // the grouped GEMM kernels (gemm16.hip: bf16 activations; gemm_a8.hip: MXFP8
 // activations with MXFP4 weights). All compute 256 x 256 tiles with 8
 // waves; they differ in the k covered per step, the MFMA shape and the
-// operand formats.
+// operand formats. The kernel with MXFP4 weights and bf16 activations also
+// runs wide tiles of 128 rows x 512 B-columns for the last M-tile of an
+// expert when it holds at most 128 rows: every wave then has a full 128 x
+// 64 block of work, where a 256-row tile would leave half the waves idle.
 #pragma once
 
 #include "common.h"
@@ -22,6 +25,8 @@ namespace {
 
 constexpr int TM = kBM;                 // 256 rows per tile
 constexpr int TN = 256;                 // B-columns per tile
+constexpr int TMW = 128;                // wide tiles: rows
+constexpr int TNW = 512;                // wide tiles: B-columns
 constexpr int kCUsPerXCD = 32;          // MI355X: 256 CUs in 8 XCDs
 constexpr int kMaxSplit = 8;            // K-parts of a split tile
 constexpr int kMinPartK = 1024;         // shortest K range of a split part
@@ -36,6 +41,7 @@ struct Args {
   const int32_t* tilemap;
   const int32_t* offsets;
   int rows, max_tiles, K, N, n_tiles_n;
+  int n_tiles_w;          // N-tiles of a wide tile row (the tile map lists wide tiles)
   const void* B0;
   const void* B1;
   const uint8_t* S0;
@@ -85,7 +91,18 @@ __device__ __forceinline__ void wait_copy_groups(int groups) {
   }
 }
 
-// Tile order, by expert: an expert's tiles are contiguous, in groups of up
+// Tile map (tilemap_kernel): [0] = regular M-tiles MR, [1] = wide M-tiles
+// MW (-1: wide tiles off, every M-tile regular), then the (expert, first
+// row) of the MR regular M-tiles in expert order and of the MW wide ones.
+// With wide tiles on, an expert of r rows has r / 256 full M-tiles, its
+// remainder r % 256 (if any) is one more regular M-tile above 128 rows and
+// a wide M-tile otherwise.
+__device__ __forceinline__ int regular_mtiles(int rows, bool wide_on) {
+  const int rem = rows % TM;
+  return rows / TM + (rem > (wide_on ? TMW : 0) ? 1 : 0);
+}
+
+// Regular tile order, by expert: an expert's tiles are contiguous, in groups of up
 // to 16 of its M-tiles; inside a group N-tile major and M-tile minor. The 32
 // workgroups an XCD runs at once then cover all M-tiles of one expert (up
 // to 16) for a few N-tiles, so each weight slab is fetched once and shared
@@ -100,10 +117,10 @@ __device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int3
   int first = 0, m = MT;
   if (tilemap) {
     const int g = t / NT;
-    const int e = tilemap[1 + 2 * g];
+    const int e = tilemap[2 + 2 * g];
     const int seg = offsets[e];
-    first = g - (tilemap[2 + 2 * g] - seg) / TM;
-    m = (offsets[e + 1] - seg + TM - 1) / TM;
+    first = g - (tilemap[3 + 2 * g] - seg) / TM;
+    m = regular_mtiles(offsets[e + 1] - seg, tilemap[1] >= 0);
   }
   const int r = t - first * NT;
   const int gi = r / (MG * NT);
@@ -113,7 +130,11 @@ __device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int3
   mt = first + gi * MG + rr % gsz;
 }
 
-// Workgroup -> (tile, k-range). Workgroup b runs on XCD b mod 8 as that
+// Workgroup -> (tile, k-range). The regular tiles, in expert_tile_of
+// order, and the wide ones (wide M-tile major, N-tile minor) are each cut
+// into 8 contiguous ranges, one per XCD; an XCD runs its regular range,
+// then its wide range (every XCD gets its share of the wide tiles).
+// Workgroup b runs on XCD b mod 8 as that
 // XCD's (b / 8)-th workgroup. An XCD's whole rounds of kCUsPerXCD tiles run
 // as whole tiles; each tile of its last, partial round is split along K
 // into S parts (S x remainder <= kCUsPerXCD, each part at least kMinPartK
@@ -125,37 +146,48 @@ __device__ __forceinline__ void expert_tile_of(int t, int MT, int NT, const int3
 // dispatched before it) adds them in part order and runs the epilogue.
 struct Job {
   int e, row0, row_end, nt, S, part, slot0, kt_begin, nk;
+  bool wide;
 };
 template <int BK>
 __device__ __forceinline__ bool schedule_tile(const Args& a, int b, Job& j) {
   const int xcd = b & 7, wi = b >> 3;
   const int MT = a.tilemap ? a.tilemap[0] : a.max_tiles;
-  const int total = MT * a.n_tiles_n;
-  const int t_lo = (int)((long long)total * xcd / 8);
-  const int t_hi = (int)((long long)total * (xcd + 1) / 8);
-  const int whole = (t_hi - t_lo) / kCUsPerXCD * kCUsPerXCD;
-  const int rem = t_hi - t_lo - whole;
+  const int MW = a.tilemap ? max(a.tilemap[1], 0) : 0;
+  const int total_reg = MT * a.n_tiles_n, total_w = MW * a.n_tiles_w;
+  const int r_lo = (int)((long long)total_reg * xcd / 8);
+  const int r_n = (int)((long long)total_reg * (xcd + 1) / 8) - r_lo;
+  const int w_lo = (int)((long long)total_w * xcd / 8);
+  const int n = r_n + (int)((long long)total_w * (xcd + 1) / 8) - w_lo;
+  const int whole = n / kCUsPerXCD * kCUsPerXCD;
+  const int rem = n - whole;
   const int nk_all = a.K / BK;
-  int tile;
+  int li;  // the tile's place in this XCD's list
   j.S = 1;
   j.part = 0;
   j.slot0 = 0;
   if (wi < whole) {
-    tile = t_lo + wi;
+    li = wi;
   } else {
     if (a.split_flags && rem > 0)
       j.S = max(1, min(min(kMaxSplit, kCUsPerXCD / rem), a.K / kMinPartK));
     const int u = wi - whole;
     if (u >= rem * j.S) return false;
-    tile = t_lo + whole + u / j.S;
+    li = whole + u / j.S;
     j.part = u % j.S;
     j.slot0 = xcd * kCUsPerXCD + (u / j.S) * (j.S - 1);
   }
   int mt;
-  expert_tile_of(tile, MT, a.n_tiles_n, a.tilemap, a.offsets, mt, j.nt);
+  j.wide = li >= r_n;
+  if (j.wide) {
+    const int u = w_lo + li - r_n;
+    mt = MT + u / a.n_tiles_w;
+    j.nt = u % a.n_tiles_w;
+  } else {
+    expert_tile_of(r_lo + li, MT, a.n_tiles_n, a.tilemap, a.offsets, mt, j.nt);
+  }
   if (a.tilemap) {
-    j.e = a.tilemap[1 + 2 * mt];
-    j.row0 = a.tilemap[2 + 2 * mt];
+    j.e = a.tilemap[2 + 2 * mt];
+    j.row0 = a.tilemap[3 + 2 * mt];
     j.row_end = a.offsets[j.e + 1];
   } else {
     j.e = 0;

@@ -22,8 +22,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Upper bound of the number of M-tiles: every kept row in a full tile plus
 // one partial tile per expert.
 inline int max_mtiles(const moe_cfg& c) { return ceil_div((long long)c.T * c.top_k, kBM) + c.E; }
-// int32 entries of the tile map: [0] = tile count, then (expert, row0) pairs.
-inline size_t tilemap_ints(const moe_cfg& c) { return 1 + 2 * (size_t)max_mtiles(c); }
+// int32 entries of the tile map: [0] = regular M-tiles, [1] = wide M-tiles
+// (-1: off), then (expert, row0) pairs of the regular, then the wide M-tiles.
+inline size_t tilemap_ints(const moe_cfg& c) { return 2 + 2 * (size_t)max_mtiles(c); }
 // The grouped GEMMs split the tiles of their last round along K: one slot
 // of 256 x 256 fp32 partial sums per split part (at most 32 per XCD), and
 // one ready flag per slot in each of two banks (gate/up, then down), both
@@ -68,11 +69,14 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
                            int32_t* offsets, int32_t* slot_pos, int32_t* perm, void* x_perm,
                            int32_t* chunk_ws, hipStream_t s);
 
-// Builds the tile map (tilemap_ints(c) int32, M-tiles of kBM rows)
+// Builds the tile map (tilemap_ints(c) int32, M-tiles of kBM rows; with
+// `wide`, an expert's last M-tile of at most kBM / 2 rows becomes a wide
+// tile of 128 rows x 512 B-columns, which the MXFP4-weight GEMM with bf16
+// activations runs)
 // from device offsets; also zeroes both banks of split flags
 // (2 kSplitSlots int32) when `flags` is not null.
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
-                          int32_t* flags, hipStream_t s);
+                          int32_t* flags, bool wide, hipStream_t s);
 
 // bf16 activations: grouped MFMA GEMMs over the tile map. A dense launch
 // (tilemap == nullptr) treats rows [0, rows) as one segment of expert 0.

@@ -10,19 +10,20 @@ from mixture_experts_layer_25_amd import synthetic as syn
 _BASE = syn.CONFIGS["mixtral"]
 
 SPLIT_CASES = {
-    # 8 experts, one M-tile each: gate/up 128 tiles (16 per XCD) and down 64
-    # (8 per XCD), K = 2048 -> 2 parts
+    # 8 experts of at most a few hundred rows: gate/up 128 tiles and down
+    # 64 (MXFP4 weights: 80 and 40, with wide tails), K = 2048 -> 2 parts
     "split2_bf16": (_BASE.replace(name="split2_bf16", T=300, D=2048, F=2048),
                     {"gate_up": 2, "down": 2}),
     "split2_mxfp4": (_BASE.replace(name="split2_mxfp4", T=300, D=2048, F=2048, wdt=syn.MXFP4),
                      {"gate_up": 2, "down": 2}),
     "split2_a8": (_BASE.replace(name="split2_a8", T=300, D=2048, F=2048, wdt=syn.MXFP4_A8),
                   {"gate_up": 2, "down": 2}),
-    # 4 experts: down 4 tiles per XCD, K = F = 8192 -> 8 parts; gate/up
-    # K = D = 1024 stays whole
+    # 4 experts of about 60 rows: down 2 tiles per XCD, K = F = 8192 -> 8
+    # parts; gate/up K = D = 1024 stays whole
     "split8_down": (_BASE.replace(name="split8_down", T=120, D=1024, E=4, F=8192),
                     {"down": 8}),
-    # 4 experts: down 8 tiles per XCD, K = F = 4096 -> 4 parts
+    # 4 experts of about 60 rows: down 4 tiles per XCD, K = F = 4096 -> 4
+    # parts
     "split4_down": (_BASE.replace(name="split4_down", T=120, D=2048, E=4, F=4096),
                     {"down": 4}),
 }

@@ -17,10 +17,15 @@ from gpu_helpers import assert_close, check_routing, gpu_forward, tol_for
 pytestmark = pytest.mark.gpu
 
 
+def _wide(cfg):
+    """Wide tiles run with MXFP4 weights and bf16 activations."""
+    return cfg.wdt == syn.MXFP4
+
+
 def _plan_S(cfg, offsets, gemm):
     swiglu = gemm == "gate_up"
     K, N = (cfg.D, cfg.F) if swiglu else (cfg.F, cfg.D)
-    return {t.S for t in tp.plan(offsets, K, N, swiglu)}
+    return {t.S for t in tp.plan(offsets, K, N, swiglu, wide=_wide(cfg))}
 
 
 @pytest.mark.parametrize("name", list(SPLIT_CASES))
@@ -88,7 +93,7 @@ def test_split_give_up_stores_nan_in_exactly_the_split_tiles(name):
     off = d["offsets"].cpu().numpy()
     A = int(off[-1])
     tiles = {g: [t for t in tp.plan(off, *((cfg.D, cfg.F) if g == "gate_up" else (cfg.F, cfg.D)),
-                                    g == "gate_up")] for g in ("gate_up", "down")}
+                                    g == "gate_up", wide=_wide(cfg))] for g in ("gate_up", "down")}
     n_split = {g: sum(t.S > 1 for t in ts) for g, ts in tiles.items()}
     assert n_split["gate_up"] + n_split["down"] > 0
     ws = moe.workspace(c, moe.WS_EXPERT_FFN, x.device)
