@@ -29,6 +29,10 @@ SMALL = {
     # the same layer with MXFP8 activation operands in the routed experts
     "fine384_mxfp4_a8": syn.small_variant(syn.CONFIGS["fine384_mxfp4_a8"], T=200, D=256, F=128,
                                           shared_F=96),
+    # 16 MXFP4 experts of 99..436 rows: full 256-row M-tiles, last M-tiles
+    # above 128 rows, and wide last M-tiles of 65..128 and of at most 64 rows
+    "mxfp4_mixed_tiles": syn.small_variant(syn.CONFIGS["fine384_mxfp4"], T=600, D=256, F=160,
+                                           E=16, shared_F=96),
 }
 
 
