@@ -6,8 +6,8 @@ or overwrites an MFMA destination register right after such a block (a
 register move, a spill), nothing guarantees the wait states the hardware
 needs, and the value read can be stale. This module compiles a HIP source
 to gfx950 assembly and reports every compiler instruction, within the first
-few after an asm block that issues MFMAs, that touches a register one of the
-block's last MFMAs writes.
+few executed after an asm block that issues MFMAs (following branches), that
+touches a register one of the block's last MFMAs writes.
 
     python -m mixture_experts_layer_25_amd.asmcheck [source.hip]
 """
@@ -37,6 +37,7 @@ def _regs(op: str) -> set:
 
 def find_hazards(asm: str) -> list[str]:
     lines = asm.split("\n")
+    labels = {l.split(":")[0]: n for n, l in enumerate(lines) if re.match(r"^\.LBB\w+:", l)}
     found = []
     func = "?"
     i = 0
@@ -69,20 +70,42 @@ def find_hazards(asm: str) -> list[str]:
                     for n in mf[-8:]:
                         dst |= _regs(body[n].split()[1].rstrip(","))
             if dst:
-                k, n = j + 1, 0
-                while n < WINDOW and k < len(lines) and ";;#ASMSTART" not in lines[k]:
-                    t = lines[k].strip()
-                    if t and not t.startswith((";", ".")):
-                        touched = set()
-                        for op in re.findall(r"[av]\[\d+:\d+\]|\b[av]\d+\b", t):
-                            touched |= _regs(op)
-                        if touched & dst:
-                            found.append(f"{func}: {t}")
-                        n += 1
-                    k += 1
+                found.extend(f"{func}: {t}" for t in _touches(lines, labels, j + 1, dst))
             i = j
         i += 1
     return found
+
+
+def _touches(lines, labels, start, dst):
+    """Instructions among the first WINDOW executed after line `start` (on
+    every path: an unconditional branch continues at its target, a
+    conditional one on both sides) that touch a register in dst; a path
+    ends at the next asm block or at s_endpgm."""
+    out, todo, seen = [], [(start, 0)], set()
+    while todo:
+        k, n = todo.pop()
+        while n < WINDOW and k < len(lines) and ";;#ASMSTART" not in lines[k]:
+            if (k, n) in seen:
+                break
+            seen.add((k, n))
+            t = lines[k].strip()
+            k += 1
+            if not t or t.startswith((";", ".")):
+                continue
+            touched = set()
+            for op in re.findall(r"[av]\[\d+:\d+\]|\b[av]\d+\b", t):
+                touched |= _regs(op)
+            if touched & dst:
+                out.append(t)
+            n += 1
+            op = t.split()[0]
+            if op == "s_endpgm":
+                break
+            if op.startswith("s_cbranch") and t.split()[-1] in labels:
+                todo.append((labels[t.split()[-1]], n))
+            elif op == "s_branch" and t.split()[-1] in labels:
+                k = labels[t.split()[-1]]
+    return out
 
 
 def compile_to_asm(src: str) -> str:

@@ -223,13 +223,11 @@ constexpr int PER16 = ACP16 + BCP16;
 constexpr int BROW16 = TN * 2;  // bytes of one B k-row
 static_assert(NST16 * SB16 == 160 * 1024, "the stages fill the LDS");
 
-template <int MODE>
-__global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
+// HALF: the wave has at most 64 rows of the tile (see gemm16_mx_body).
+template <int MODE, bool HALF>
+__device__ __forceinline__ void gemm16_body(const Args& a, const Job& jb, unsigned char* smem) {
   constexpr int A_BYTES = A16_BYTES, SB = SB16, NST = NST16, PER = PER16;
   constexpr int BROW = BROW16, COLS = TN;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NST16 * SB16];
-  Job jb;
-  if (!schedule_tile<BK16>(a, blockIdx.x, jb)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;   // 0..7
@@ -392,6 +390,25 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
                  [bb1] "v"(b_addr[1] + (SO)), [bb2] "v"(b_addr[2] + (SO)),            \
                  [bo] "n"(4 * BROW), __VA_ARGS__                                     \
                : "memory", "m0")
+  // the same reads and copies without the MFMAs (HALF)
+#define HALF_R(X0, X1, X2, X3, X4, X5, X6, X7, X8, X9, X10, X11, X12, X13, X14, X15)   \
+  X0 X1 X2 X3 X4 X5 X6 X7 X8 X9 X10 X11 X12 X13 X14 X15
+#define HALF_RX(...) HALF_R(__VA_ARGS__)
+#define H2R(SO, C0, C1, C2, C3, ...)                                                  \
+  asm volatile(HALF_RX(RDA("np0", "0"), C0, RDA("np1", "1024"), RDB0, RDA("np2", "2048"), C1, \
+                       RDA("np3", "3072"), RDB1, C2, "", "", RDB2, C3, "", "", "")     \
+               "s_waitcnt lgkmcnt(0)"                                                \
+               : [np0] "=&v"(p0), [np1] "=&v"(p1), [np2] "=&v"(p2), [np3] "=&v"(p3),  \
+                 BPIN                                                                \
+               : [aa] "v"(a_addr + (SO)), [bb0] "v"(b_addr[0] + (SO)),                \
+                 [bb1] "v"(b_addr[1] + (SO)), [bb2] "v"(b_addr[2] + (SO)),            \
+                 [bo] "n"(4 * BROW), __VA_ARGS__                                     \
+               : "memory", "m0")
+#define H2_ANY(...)                                                                  \
+  do {                                                                               \
+    if constexpr (HALF) H2R(__VA_ARGS__);                                            \
+    else H2(__VA_ARGS__);                                                            \
+  } while (0)
   // the last second half: MFMAs only, then the result wait states
 #define H2_LAST()                                                                    \
   asm volatile("s_nop 4\n\t" HALF("", "", "", "", "", "", "", "", "", "", "", "", "", "", "", "") \
@@ -451,7 +468,7 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
         uint64_t gb1 = (uint64_t)(b_g[1] + (size_t)is * BK16 * N * 2);
         H1(so, CP(0), "", CP(1), "", [g0] "v"(ga0), [g1] "v"(ga1), [m0] "s"(lds_a + si),
            [m1] "s"(lds_a + si + 8192));
-        H2(so1, CP(0), "", CP(1), "", [g0] "v"(gb0), [g1] "v"(gb1), [m0] "s"(lds_b + si),
+        H2_ANY(so1, CP(0), "", CP(1), "", [g0] "v"(gb0), [g1] "v"(gb1), [m0] "s"(lds_b + si),
            [m1] "s"(lds_b + si + 1024));
         // step kt + 1: after the barrier, copies of step kt + NST into the
         // stage of step kt
@@ -464,7 +481,7 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
         ga1 = (uint64_t)(a_g[1] + is * BK16);
         gb0 = (uint64_t)(b_g[0] + (size_t)is * BK16 * N * 2);
         gb1 = (uint64_t)(b_g[1] + (size_t)is * BK16 * N * 2);
-        H2(so2, CP(0), CP(1), CP(2), CP(3), [g0] "v"(ga0), [g1] "v"(ga1), [g2] "v"(gb0),
+        H2_ANY(so2, CP(0), CP(1), CP(2), CP(3), [g0] "v"(ga0), [g1] "v"(ga1), [g2] "v"(gb0),
            [g3] "v"(gb1), [m0] "s"(lds_a + si1), [m1] "s"(lds_a + si1 + 8192),
            [m2] "s"(lds_b + si1), [m3] "s"(lds_b + si1 + 1024));
         so = so2;
@@ -482,17 +499,21 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
         asm volatile("" ::: "memory");
       }
       if (is < nk) issue(kt_begin + is, si);
-      H2(so1, "", "", "", "", NOCOPY);
+      H2_ANY(so1, "", "", "", "", NOCOPY);
       so = so1;
       si = next_stage(si);
     }
     // last step
     H1(so, "", "", "", "", NOCOPY);
-    H2_LAST();
+    if constexpr (!HALF) H2_LAST();
   }
   // the last MFMAs finish writing the accumulators before any VALU reads them
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #undef H2_LAST
+#undef H2_ANY
+#undef H2R
+#undef HALF_RX
+#undef HALF_R
 #undef H2
 #undef H1
 #undef NOCOPY
@@ -513,6 +534,18 @@ __global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
 #undef M16
 
   finish_tile16<MODE, false>(a, jb, acc, smem, wave, lane, tid, n0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NST16 * SB16];
+  Job jb;
+  if (!schedule_tile<BK16>(a, blockIdx.x, jb)) return;
+  const int wm = threadIdx.x >> 8;  // the wave's row half
+  if (__builtin_amdgcn_readfirstlane(jb.row_end - jb.row0 - 128 * wm) <= 64)
+    gemm16_body<MODE, true>(a, jb, smem);
+  else
+    gemm16_body<MODE, false>(a, jb, smem);
 }
 
 // ---- MXFP4 weights. A and the pipeline as above; B stage per step: the 16
@@ -543,9 +576,10 @@ struct ShapeMx {
 constexpr int kLdsMx = ShapeMx<false>::NST * ShapeMx<false>::SB;
 static_assert(ShapeMx<true>::NST * ShapeMx<true>::SB <= kLdsMx, "wide stages fit");
 
-// HALF (wide tiles of at most 64 rows): row tiles 4-7 (A set Q) lie past the
-// segment, so the second half of every step keeps its reads and copies but
-// runs no MFMAs.
+// HALF (a wave with at most 64 rows of the tile): its row tiles 4-7 (A set
+// Q) lie past the segment, so the second half of every step keeps its reads
+// and copies but runs no MFMAs. The waves of a tile may take different
+// variants: they pass the same barriers.
 template <int MODE, bool WIDE, bool HALF>
 __device__ __forceinline__ void gemm16_mx_body(const Args& a, const Job& jb, unsigned char* smem) {
   using SH = ShapeMx<WIDE>;
@@ -835,13 +869,15 @@ __global__ __launch_bounds__(512) void gemm16_mx_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsMx];
   Job jb;
   if (!schedule_tile<BK16>(a, blockIdx.x, jb)) return;
-  if (__builtin_amdgcn_readfirstlane((int)jb.wide)) {
-    if (__builtin_amdgcn_readfirstlane(jb.row_end - jb.row0) <= 64)
-      gemm16_mx_body<MODE, true, true>(a, jb, smem);
-    else
-      gemm16_mx_body<MODE, true, false>(a, jb, smem);
+  const bool wide = __builtin_amdgcn_readfirstlane((int)jb.wide) != 0;
+  const int wm = wide ? 0 : (int)(threadIdx.x >> 8);  // the wave's row half
+  const bool half = __builtin_amdgcn_readfirstlane(jb.row_end - jb.row0 - 128 * wm) <= 64;
+  if (wide) {
+    if (half) gemm16_mx_body<MODE, true, true>(a, jb, smem);
+    else gemm16_mx_body<MODE, true, false>(a, jb, smem);
   } else {
-    gemm16_mx_body<MODE, false, false>(a, jb, smem);
+    if (half) gemm16_mx_body<MODE, false, true>(a, jb, smem);
+    else gemm16_mx_body<MODE, false, false>(a, jb, smem);
   }
 }
 

@@ -46,6 +46,33 @@ def test_checker_flags_reads_right_after_mfma_blocks():
     assert "a3" in found[0] and "v[44:47]" in found[1] and "v79" in found[2]
 
 
+BRANCHES = """
+_Zkernel:
+	;;#ASMSTART
+	v_mfma_f32_16x16x32_bf16 v[2:5], v[6:9], v[10:13], v[2:5]
+	;;#ASMEND
+	s_cbranch_scc1 .LBB0_2
+	s_branch .LBB0_3
+.LBB0_1:
+	v_mov_b32_e32 v20, v2
+.LBB0_2:
+	v_mov_b32_e32 v21, v3
+	s_endpgm
+.LBB0_3:
+	v_mov_b32_e32 v22, v4
+	s_endpgm
+	v_mov_b32_e32 v23, v5
+"""
+
+
+def test_checker_follows_branches():
+    # both branch targets are executed after the block (v3 and v4 read); the
+    # block skipped by the unconditional branch (v2) and code after an
+    # s_endpgm (v5) are not
+    found = asmcheck.find_hazards(BRANCHES)
+    assert sorted(found) == ["_Zkernel: v_mov_b32_e32 v21, v3", "_Zkernel: v_mov_b32_e32 v22, v4"]
+
+
 @pytest.mark.skipif(not os.path.exists(asmcheck.HIPCC) and shutil.which("hipcc") is None,
                     reason="hipcc not available")
 @pytest.mark.parametrize("name", asmcheck.SOURCES)
