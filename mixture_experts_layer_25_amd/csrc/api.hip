@@ -155,9 +155,9 @@ ForwardWs carve_forward(const moe_cfg& c, void* ws) {
   return f;
 }
 
-// MXFP4 weights with bf16 activations run an expert's last M-tile of at
-// most 128 rows as a wide tile (gemm16_mx_kernel); the other GEMMs do not.
-bool wide_tiles(const moe_cfg& c) { return is_mx(c) && !is_a8(c); }
+// MXFP4 weights (with bf16 or MXFP8 activations) run an expert's last
+// M-tile of at most 128 rows as a wide tile; bf16 weights do not.
+bool wide_tiles(const moe_cfg& c) { return is_mx(c); }
 
 moe::GemmProblem routed_problem(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap) {
   moe::GemmProblem g{};

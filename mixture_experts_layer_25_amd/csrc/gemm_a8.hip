@@ -68,6 +68,28 @@ constexpr int LDS8 = AS_OFF + 3 * ASG_BYTES;  // 134.5 KB of the 160 KB LDS
 static_assert(LDS8 <= 160 * 1024, "LDS");
 static_assert(LDS8 >= 8 * 128 * 128, "the epilogue stages 16 KB per wave");
 
+// Wide tiles (an expert's last M-tile of at most 128 rows): 128 rows x 512
+// B-columns, the 8 waves side by side on the same rows. Stage: 8 KB of A
+// codes, 16 KB of B codes, 1 KB of B scales; A-scale groups of 2 KB.
+template <bool WIDE>
+struct ShapeA8 {
+  static constexpr int ROWS = WIDE ? TMW : TM;
+  static constexpr int COLS = WIDE ? TNW : TN;
+  static constexpr int A_BYTES = ROWS * BK8;
+  static constexpr int BC_BYTES = 2 * COLS * 16;
+  static constexpr int BS_BYTES = 2 * COLS;
+  static constexpr int SB = A_BYTES + BC_BYTES + BS_BYTES;
+  static constexpr int ASG = ROWS * 16;
+  static constexpr int AS_OFF = NST8 * SB;
+  static constexpr int LDS = AS_OFF + 3 * ASG;
+  static constexpr int ACP = ROWS * 4 / 512;    // A copies per thread and step
+  static constexpr int BCP = COLS * 2 / 512;    // B code copies per thread and step
+  static constexpr int NBS = COLS / 128;        // waves copying B scales (one dword a lane)
+  static constexpr int NAS = ROWS / 64;         // waves copying A-scale groups
+};
+static_assert(ShapeA8<false>::LDS == LDS8, "the regular shape is the one above");
+static_assert(ShapeA8<true>::LDS <= LDS8 && ShapeA8<true>::LDS >= 8 * 128 * 128, "wide LDS");
+
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -128,28 +150,28 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __rest
   scales[GROUPED ? grouped_scale(b / KB, (int)(b % KB), rows) : (size_t)b] = (uint8_t)s;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS8];
+template <int MODE, bool WIDE>
+__device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsigned char* smem) {
+  using SH = ShapeA8<WIDE>;
+  constexpr int A8_BYTES = SH::A_BYTES, B8C_BYTES = SH::BC_BYTES, SB8 = SH::SB;
+  constexpr int ASG_BYTES = SH::ASG, AS_OFF = SH::AS_OFF, COLS = SH::COLS;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2;  // row half
-  const int wn = wave & 3;   // column quarter
+  const int wm = WIDE ? 0 : wave >> 2;   // row half
+  const int wn = WIDE ? wave : wave & 3; // column block
 
-  Job jb;
-  if (!schedule_tile<BK8>(a, blockIdx.x, jb)) return;
   const int e = jb.e, row0 = jb.row0, row_end = jb.row_end, nt = jb.nt;
   const int kt_begin = jb.kt_begin, nk = jb.nk;
   const int K = a.K, N = a.N, KB = K / 32;
-  const int n0 = MODE == MODE_SWIGLU ? nt * 128 : nt * 256;
+  const int n0 = MODE == MODE_SWIGLU ? nt * (COLS / 2) : nt * COLS;
 
-  // weight column of tile column c (0..255), as in the bf16 kernel
+  // weight column of tile column c (0..COLS-1), as in the bf16 kernel
   auto b_column = [&](int c, bool& up) __attribute__((always_inline)) {
     int col;
     if (MODE == MODE_SWIGLU) {
-      up = c >= 128;
-      col = n0 + (c & 127);
+      up = c >= COLS / 2;
+      col = n0 + (c & (COLS / 2 - 1));
     } else {
       up = false;
       col = n0 + c;
@@ -162,42 +184,48 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
     return r;
   };
 
-  // ---- copy sources and destinations. Per step and thread: two 16-byte
-  // pieces of A and one of B codes; waves 0 and 1 also copy the step's two
-  // blocks of B scales (one dword per lane: 4 columns). The A scales come
-  // in groups of 8 steps (16 bytes per row, grouped layout): wave w < 4
-  // copies its 64 rows of group G + 2 at the step of group G whose index
-  // within the group is w, into a ring of 3 group buffers; the first
-  // groups of the tile's k-range are copied before the loop.
+  // ---- copy sources and destinations. Per step and thread: ACP 16-byte
+  // pieces of A and BCP of B codes (regular: 2 and 1, wide: 1 and 2); the
+  // first NBS waves also copy the step's two blocks of B scales (one dword
+  // per lane: 4 columns). The A scales come in groups of 8 steps (16 bytes
+  // per row, grouped layout): wave w < NAS copies its 64 rows of group G + 2
+  // at the step of group G whose index within the group is w, into a ring
+  // of 3 group buffers; the first groups of the tile's k-range are copied
+  // before the loop.
   const uint8_t* A = static_cast<const uint8_t*>(a.A);
-  const uint8_t* a_g[2];
+  const uint8_t* a_g[SH::ACP];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < SH::ACP; ++r) {
     const int p = 512 * r + tid, m = p >> 2, q = (p & 3) ^ swz4(m);
     a_g[r] = A + (size_t)a_row(m) * K + kt_begin * BK8 + 16 * q;
   }
-  const int blk = tid >> 8, c = tid & 255;
-  const uint8_t* bc_g;
-  {
+  // B code copy r of thread t: block (regular) t / 256 or (wide) r, tile
+  // column t % 256 or t
+  const uint8_t* bc_g[SH::BCP];
+#pragma unroll
+  for (int r = 0; r < SH::BCP; ++r) {
+    const int blk = WIDE ? r : tid >> 8, c = WIDE ? tid : tid & 255;
     bool up;
     const int col = b_column(c, up);
     const size_t bi = ((size_t)e * KB + 2 * kt_begin + blk) * N + col;
-    bc_g = static_cast<const uint8_t*>(up ? a.B1 : a.B0) + bi * 16;
+    bc_g[r] = static_cast<const uint8_t*>(up ? a.B1 : a.B0) + bi * 16;
   }
   const size_t bc_step = (size_t)2 * N * 16;
-  // B scales: wave b < 2 copies block b of each step, lane l the 4 columns
-  // of tile columns 4l.. (SwiGLU: gate for l < 32, up for l >= 32)
+  // B scales: wave w < NBS copies block w / (NBS / 2) of each step, lane l
+  // the 4 columns of tile columns 4 c4.., c4 = 64 (w % (NBS / 2)) + l
+  // (SwiGLU: gate for c4 < COLS / 8, up above)
   const uint8_t* bs_g = nullptr;
-  if (wave < 2) {
-    const bool up = MODE == MODE_SWIGLU && lane >= 32;
-    int col = MODE == MODE_SWIGLU ? n0 + 4 * (lane & 31) : n0 + 4 * lane;
+  if (wave < SH::NBS) {
+    const int c4 = 64 * (wave % (SH::NBS / 2)) + lane, blk = wave / (SH::NBS / 2);
+    const bool up = MODE == MODE_SWIGLU && c4 >= COLS / 8;
+    int col = MODE == MODE_SWIGLU ? n0 + 4 * (c4 & (COLS / 8 - 1)) : n0 + 4 * c4;
     if (col >= N) col = 0;  // any valid columns; never stored
-    bs_g = (up ? a.S1 : a.S0) + ((size_t)e * KB + 2 * kt_begin + wave) * N + col;
+    bs_g = (up ? a.S1 : a.S0) + ((size_t)e * KB + 2 * kt_begin + blk) * N + col;
   }
   const size_t bs_step = (size_t)2 * N;
   // A scales: row 64 w + lane of the tile, grouped layout
   const long long sa_rows = a.gather ? a.gather_rows : a.rows;
-  const uint8_t* as_g = wave < 4 ? a.SA + (size_t)a_row(64 * wave + lane) * 16 : nullptr;
+  const uint8_t* as_g = wave < SH::NAS ? a.SA + (size_t)a_row(64 * wave + lane) * 16 : nullptr;
   const int g_last = (kt_begin + nk - 1) / kSG;  // last group of the k-range
   auto issue_group = [&](int g) __attribute__((always_inline)) {
     g = min(g, g_last);  // past the range: copy the last group again (same bytes)
@@ -206,17 +234,19 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
   auto issue = [&](int kt, uint32_t so) __attribute__((always_inline)) {
     unsigned char* st = smem + so;
     const int k = kt - kt_begin;
-    dma16(a_g[0] + k * BK8, st + wave * 1024);
-    dma16(a_g[1] + k * BK8, st + 8192 + wave * 1024);
-    dma16(bc_g + k * bc_step, st + A8_BYTES + wave * 1024);
-    if (wave < 2) dma4(bs_g + k * bs_step, st + A8_BYTES + B8C_BYTES + wave * 256);
+#pragma unroll
+    for (int r = 0; r < SH::ACP; ++r) dma16(a_g[r] + k * BK8, st + 8192 * r + wave * 1024);
+#pragma unroll
+    for (int r = 0; r < SH::BCP; ++r)
+      dma16(bc_g[r] + k * bc_step, st + A8_BYTES + 8192 * r + wave * 1024);
+    if (wave < SH::NBS) dma4(bs_g + k * bs_step, st + A8_BYTES + B8C_BYTES + wave * 256);
   };
-  const int per = wave < 2 ? 4 : 3;  // this wave's copies per step
+  const int per = SH::ACP + SH::BCP + (wave < SH::NBS ? 1 : 0);  // this wave's copies per step
 
   int bcol[2];
   if (MODE == MODE_SWIGLU) {
     bcol[0] = 32 * wn;
-    bcol[1] = 128 + 32 * wn;
+    bcol[1] = COLS / 2 + 32 * wn;
   } else {
     bcol[0] = 64 * wn;
     bcol[1] = 64 * wn + 32;
@@ -244,8 +274,8 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = bcol[j] + lrow;
-      bc_a[j] = base + A8_BYTES + h * 4096 + col * 16;
-      bs_a[j] = base + A8_BYTES + B8C_BYTES + h * 256 + col;
+      bc_a[j] = base + A8_BYTES + h * (COLS * 16) + col * 16;
+      bs_a[j] = base + A8_BYTES + B8C_BYTES + h * COLS + col;
     }
   }
   // A-scale offset of absolute step t: group buffer (t / 8) % 3, 2 bytes a step
@@ -351,17 +381,17 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
   do {                                                                               \
     int n = per * (min(nk - 1, kt + NST8 - 1) - min(kt + 1, nk - 1));                \
     const int lo = max(0, kt - (NST8 - 1)), hi = kt - 1;                             \
-    if (wave < 4 && hi >= lo)                                                        \
+    if (wave < SH::NAS && hi >= lo)                                                  \
       n += ((wave - (kt_begin + lo) % kSG + kSG) % kSG) <= hi - lo;                  \
     wait_vmcnt_dyn(n);                                                               \
     __builtin_amdgcn_s_barrier();                                                    \
     asm volatile("" ::: "memory");                                                   \
     if (kt + NST8 < nk) issue(kt_begin + kt + NST8, so);                             \
-    if (wave < 4 && (kt_begin + kt) % kSG == wave) issue_group((kt_begin + kt) / kSG + 2); \
+    if (wave < SH::NAS && (kt_begin + kt) % kSG == wave) issue_group((kt_begin + kt) / kSG + 2); \
   } while (0)
 
   // the first A-scale groups, then the copies of the first NST8 steps
-  if (wave < 4) {
+  if (wave < SH::NAS) {
     const int g0 = kt_begin / kSG;
     issue_group(g0);
     issue_group(g0 + 1);
@@ -478,6 +508,17 @@ __global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
   }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm_a8_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS8];
+  Job jb;
+  if (!schedule_tile<BK8>(a, blockIdx.x, jb)) return;
+  // (Half-row waves skipping the MFMAs of rows 64-127, as in gemm16.hip,
+  // made this kernel's gate/up 14 % slower; not used here.)
+  if (__builtin_amdgcn_readfirstlane((int)jb.wide)) gemm_a8_body<MODE, true>(a, jb, smem);
+  else gemm_a8_body<MODE, false>(a, jb, smem);
+}
+
 }  // namespace
 
 hipError_t launch_quant_mxfp8(const void* x, long long rows, int K, uint8_t* codes, uint8_t* scales,
@@ -504,8 +545,8 @@ hipError_t launch_gemm_a8(const GemmProblem& p, bool swiglu, hipStream_t s) {
   a.max_tiles = p.max_tiles;
   a.K = p.K;
   a.N = p.N;
-  a.n_tiles_n = swiglu ? ceil_div(p.N, 128) : ceil_div(p.N, 256);
-  a.n_tiles_w = 1;  // no wide tiles: the tile map is built without them
+  a.n_tiles_n = swiglu ? ceil_div(p.N, TN / 2) : ceil_div(p.N, TN);
+  a.n_tiles_w = swiglu ? ceil_div(p.N, TNW / 2) : ceil_div(p.N, TNW);
   a.split_ws = p.split_ws;
   a.split_flags = p.split_flags;
   a.split_wait = p.split_wait;

@@ -66,7 +66,7 @@ def stratified_tokens(cfg: syn.Config, idx: np.ndarray, slot_pos: np.ndarray,
     if cfg.act != syn.F32:
         for swiglu in (True, False):
             K, N = (cfg.D, cfg.F) if swiglu else (cfg.F, cfg.D)
-            for t in tp.plan(offsets, K, N, swiglu, wide=cfg.wdt == syn.MXFP4):
+            for t in tp.plan(offsets, K, N, swiglu, wide=syn.is_mx(cfg.wdt)):
                 if t.S > 1:
                     picks.add(int(perm[t.row0]))
     return np.array(sorted(picks), np.int32)

@@ -31,5 +31,5 @@ def test_split_cases_split():
         for gemm, S in want.items():
             swiglu = gemm == "gate_up"
             K, N = (cfg.D, cfg.F) if swiglu else (cfg.F, cfg.D)
-            got = {t.S for t in tp.plan(off, K, N, swiglu, wide=cfg.wdt == syn.MXFP4)}
+            got = {t.S for t in tp.plan(off, K, N, swiglu, wide=syn.is_mx(cfg.wdt))}
             assert S in got, (name, gemm, got)

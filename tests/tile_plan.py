@@ -11,8 +11,8 @@ contiguous ranges (one per XCD, which runs its regular range, then its wide
 range) and the split along K of each tile of an XCD's last, partial round of
 32. Tests use it to choose shapes where tiles really are split and
 to know which output rows and columns each split tile owns; it computes no
-layer arithmetic. Wide tiles are on for MXFP4 weights with bf16 activations
-and off otherwise.
+layer arithmetic. Wide tiles are on for MXFP4 weights and off for bf16
+weights.
 """
 from __future__ import annotations
 
