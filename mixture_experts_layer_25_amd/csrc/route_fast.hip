@@ -20,7 +20,8 @@
 //              k-th largest; candidates = experts with ka_e >= A - 2 eps_t.
 //   4. exact:  the exact chains of the candidates only.
 //   5. select: top k of the candidates' exact keys, ties to the lower
-//              index, and the weights, by the same code as the exact router.
+//              index, and the weights, by the exact router's order and
+//              gate_weight.
 //
 // The bound. Let c_e be the exact chain (the defined logit) and t_e the
 // real dot product. For an fp32 FMA chain |c_e - t_e| <= g_D sum_d |x_d
@@ -284,34 +285,24 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
   const double nxt = nx2[t];
   const double N = __longlong_as_double((long long)wmax[0]);
   const double R = __longlong_as_double((long long)wmax[1]);
-  // the k-th largest approximate key (k rounds of a butterfly arg-max)
-  float A = 0.0f;
-  bool left[NJ];
+  // the k-th largest approximate key: the largest order-preserving code U
+  // of a key such that at least k keys have codes >= U, found bit by bit
+  // from the top (every count is a sum of ballots, uniform across the wave)
+  uint32_t code[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) left[j] = avail[j];
-  for (int s = 0; s < k; ++s) {
-    float bk = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (left[j] && (ka[j] > bk || (ka[j] == bk && lane + 64 * j < bi))) {
-        bk = ka[j];
-        bi = lane + 64 * j;
-      }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ok = __shfl_xor(bk, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ok > bk || (ok == bk && oi < bi)) {
-        bk = ok;
-        bi = oi;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (lane + 64 * j == bi) left[j] = false;
-    A = bk;
+  for (int j = 0; j < NJ; ++j) {
+    const uint32_t b = __float_as_uint(ka[j]);
+    code[j] = avail[j] ? ((b >> 31) ? ~b : (b | 0x80000000u)) : 0u;
   }
+  uint32_t U = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = U | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(code[j] >= c));
+    if (cnt >= k) U = c;
+  }
+  const float A = __uint_as_float((U >> 31) ? (U & 0x7FFFFFFFu) : ~U);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   // eps_t and the threshold, in double (cg = 5 g_D (1 + 2^-8), from the host)
@@ -493,13 +484,51 @@ __global__ __launch_bounds__(512) void screen_exact_kernel(
   }
 }
 
-// ---- 5. selection among the candidates (one wave per token): their exact
-// keys (logit + bias) and logits, k rounds of a butterfly arg-max (a larger
-// key wins, an equal key goes to the lower expert index), weights by
-// gate_weight as in the exact router (m = the largest key; softmax is
-// always renormalised here)
-// (NJ columns of 64 candidates: the first launch takes every token with at
-// most 64 candidates, the second, with NJ = 16, the others)
+// ---- 5. selection among the candidates (one wave per token): a larger key
+// (logit + bias) ranks first, an equal key goes to the lower expert index,
+// as in the exact router; the candidates of rank 0 .. k-1 are selected in
+// that order, with weights by gate_weight (m = the largest key; softmax is
+// always renormalised here) and their sum taken in selection order.
+// Tokens with at most 64 candidates: lane i holds candidate i and counts the
+// candidates ahead of it (its rank).
+__global__ __launch_bounds__(256) void screen_select64_kernel(
+    const int16_t* __restrict__ cand, const int32_t* __restrict__ ncand,
+    const float* __restrict__ exl, const float* __restrict__ exk, int T, int E, int k,
+    int gating, int renorm, int32_t* __restrict__ idx, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int n = ncand[t];
+  if (n > 64) return;  // the other launch's token
+  const bool avail = lane < n;
+  const size_t q = (size_t)t * E + lane;
+  const int ex = avail ? cand[q] : 0x7FFFFFFF;
+  const float lgt = avail ? exl[q] : 0.0f;
+  const float key = avail ? exk[q] : -INFINITY;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const float kj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key), j));
+    const int ej = __builtin_amdgcn_readlane(ex, j);
+    rank += (kj > key || (kj == key && ej < ex)) ? 1 : 0;
+  }
+  const bool sel = avail && rank < k;
+  // n >= k >= 1: the k largest approximate keys are always candidates
+  const int l0 = __ffsll(__ballot(sel && rank == 0)) - 1;
+  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key), l0));
+  const float wv = sel ? gate_weight(gating, renorm, key, lgt, m, 1.0f) : 0.0f;
+  float wsum = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    const int lr = __ffsll(__ballot(sel && rank == r)) - 1;
+    wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), lr));
+  }
+  if (sel) {
+    idx[(size_t)t * k + rank] = ex;
+    w[(size_t)t * k + rank] = renorm ? wv / wsum : wv;
+  }
+}
+
+// Tokens with more than 64 candidates (NJ columns of 64): k rounds of a
+// butterfly arg-max under the same order
 template <int NJ>
 __global__ __launch_bounds__(256) void screen_select_kernel(
     const int16_t* __restrict__ cand, const int32_t* __restrict__ ncand,
@@ -509,7 +538,7 @@ __global__ __launch_bounds__(256) void screen_select_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int n = ncand[t];
-  if ((n > 64 * NJ) || (NJ > 1 && n <= 64)) return;  // the other launch's token
+  if (n > 64 * NJ || n <= 64) return;  // the other launch's token
   float key[NJ], lgt[NJ];
   int ex[NJ];
   bool avail[NJ];
@@ -600,8 +629,8 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   else screen_cand_kernel<16><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
   screen_exact_kernel<kExER><<<dim3(ceil_div(T, kExTB), ceil_div(E, kExER)), 512, 0, s>>>(
       xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
-  screen_select_kernel<1><<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
-                                              c.gating, c.renorm, idx, w);
+  screen_select64_kernel<<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
+                                            c.gating, c.renorm, idx, w);
   screen_select_kernel<16><<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
                                                  c.gating, c.renorm, idx, w);
   return hipGetLastError();
