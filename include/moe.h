@@ -171,7 +171,7 @@ int moe_route(const moe_cfg* cfg, const void* x, const float* W_r, const float* 
  * among them ("ops-transformer" pitfall 3: the router is FP32; its
  * performance comparison counts routing among the overheads). Only their
  * exact chains run; selection and weights then use the exact router's
- * code. Used with bf16 activations, E >= 256 and any gating except softmax
+ * code. Used with bf16 activations, E >= 128 and any gating except softmax
  * without renormalisation; otherwise this call runs the exact router
  * (workspace size 0). Workspace: MOE_WS_ROUTE. moe_forward takes this path
  * whenever it applies. */

@@ -43,6 +43,7 @@
 
 #include "common.h"
 #include "gating.h"
+#include "gemm_tile.h"
 #include "launch.h"
 
 namespace moe {
@@ -53,8 +54,12 @@ typedef __bf16 bf16v8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMaxK = 16;
 constexpr int kScrTM = 64;    // screen tile: tokens (experts: 64 or 128)
-constexpr int kExTB = 256;    // exact chains: tokens per workgroup
-constexpr int kExER = 96;     // exact chains: experts per workgroup
+// exact chains: tokens x experts per workgroup (16384 tokens x 384
+// experts: 64 x 4 workgroups; 8192 x 128: 128 x 4)
+struct ExTile {
+  int tb, er;
+};
+inline ExTile ex_tile(int E) { return E >= 256 ? ExTile{256, 96} : ExTile{64, 32}; }
 constexpr int kExDK = 64;     // exact chains: d per staged chunk
 
 struct ScreenWs {
@@ -92,7 +97,8 @@ ScreenWs carve(const moe_cfg& c, void* base) {
   w.exl = reinterpret_cast<float*>(take(TE * 4));
   w.exk = reinterpret_cast<float*>(take(TE * 4));
   w.gpairs = reinterpret_cast<int32_t*>(
-      take((size_t)ceil_div(c.T, kExTB) * kExTB * ceil_div(c.E, kExER) * kExER * 4));
+      take((size_t)ceil_div(c.T, ex_tile(c.E).tb) * ex_tile(c.E).tb * ceil_div(c.E, ex_tile(c.E).er) *
+           ex_tile(c.E).er * 4));
   w.bytes = align_up(off, 256);
   return w;
 }
@@ -167,46 +173,76 @@ __global__ __launch_bounds__(256) void screen_norms_kernel(const float* __restri
 }
 
 // ---- 2. screen: S = x . bf16(W_r) on v_mfma_f32_16x16x32_bf16. Tile 64
-// tokens x TN = 128 experts, 4 waves, wave w owns experts (TN/4) w .. of
-// the tile (4 x TN/64 MFMA tiles). Operands staged in LDS per 32-k step (A rows and
-// W^T rows, 64 bytes each, read as 16-byte fragments; k-group g of row r at
-// slot g ^ ((r >> 2) & 3), so that the 16 lanes of a read pass, rows r..r+15
-// of one k-group, hit 16 distinct 16-byte bank groups), double-buffered
-// through registers. Lane l supplies row l%16 of A and column l%16 of B with
-// k = 8 (l/16) .. +7 and holds rows 4 (l/16) + r of column l%16 of the 16 x
-// 16 result. The workgroups of the first expert tile also sum x_t^2 in
-// double (each staging thread over its 8 columns of every step, then the 4
-// threads of a row in a fixed order).
+// tokens x TN experts (128, or 64 for at most 128 experts), 4 waves, wave w
+// owns experts (TN/4) w .. of the tile (4 x TN/64 MFMA tiles). Operands go
+// straight from global memory to LDS (global_load_lds, 16 bytes a lane) in
+// steps of 32 k, NS steps in a ring with NS - 1 in flight; a step holds 64
+// A rows and TN W^T rows of 64 bytes each, k-group g of row r at slot
+// g ^ ((r >> 2) & 3) (the lane that copies a slot fetches that k-group), so
+// that the 16 lanes of a fragment read, rows r..r+15 of one k-group, hit 16
+// distinct 16-byte bank groups. Lane l supplies row l%16 of A and column
+// l%16 of B with k = 8 (l/16) .. +7 and holds rows 4 (l/16) + r of column
+// l%16 of the 16 x 16 result. The workgroups of the first expert tile also
+// sum x_t^2 in double: wave w over rows 16 w .. 16 w + 15 of its A
+// fragments, then the 4 lanes of a row.
 template <int TN>
 __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ whi,
                                                           int T, int D, int E,
                                                           float* __restrict__ S,
                                                           double* __restrict__ nx2) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kScrTM][32];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN][32];
-  constexpr int NJ = TN / 64;  // 16-column MFMA tiles per wave
+  constexpr int NS = 4;                        // ring of steps (48 or 32 KB)
+  constexpr int AB = kScrTM * 64, SB = AB + TN * 64;
+  constexpr int PER = 1 + TN / 64;             // 16-byte copies per thread per step
+  constexpr int NJ = TN / 64;                  // 16-column MFMA tiles per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kScrTM, e0 = blockIdx.y * TN;
-  const int ar = tid >> 2, ak = tid & 3;
-  const int aslot = 8 * (ak ^ ((ar >> 2) & 3));
-  const uint16_t* ag = x + (size_t)min(t0 + ar, T - 1) * D + 8 * ak;
-  const uint16_t* bg0 = whi + (size_t)min(e0 + ar, E - 1) * D + 8 * ak;
-  const uint16_t* bg1 = whi + (size_t)min(e0 + 64 + ar, E - 1) * D + 8 * ak;
+  // the copies: this lane's row of A (and of each W^T quarter) and k-group
+  const int cr = 16 * wave + (lane >> 2), cs = lane & 3;
+  const uint16_t* ag = x + (size_t)min(t0 + cr, T - 1) * D + 8 * (cs ^ ((cr >> 2) & 3));
+  const uint16_t* bg[NJ];
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    const int r = 64 * q + cr;
+    bg[q] = whi + (size_t)min(e0 + r, E - 1) * D + 8 * (cs ^ ((r >> 2) & 3));
+  }
+  const int nk = D / 32;
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    unsigned char* st = sm + (kt % NS) * SB;
+    dma16(ag + 32 * kt, st + 1024 * wave);
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) dma16(bg[q] + 32 * kt, st + AB + 4096 * q + 1024 * wave);
+  };
   const bool norm = blockIdx.y == 0;
   double sq = 0.0;
-  uint4 ra, rb0, rb1;
-  auto load = [&](int kt) __attribute__((always_inline)) {
-    ra = *reinterpret_cast<const uint4*>(ag + kt * 32);
-    rb0 = *reinterpret_cast<const uint4*>(bg0 + kt * 32);
-    if (TN == 128) rb1 = *reinterpret_cast<const uint4*>(bg1 + kt * 32);
-  };
-  auto store = [&](int buf) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(&As[buf][ar][aslot]) = ra;
-    *reinterpret_cast<uint4*>(&Bs[buf][ar][aslot]) = rb0;
-    if (TN == 128) *reinterpret_cast<uint4*>(&Bs[buf][64 + ar][aslot]) = rb1;
+  f32x4_t acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int l16 = lane & 15, g = lane >> 4;
+  const int rs = 16 * (g ^ ((l16 >> 2) & 3));  // rows 16 i + l16 share bits 2-3 of l16
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_copy_groups<PER>(min(NS - 2, nk - 1 - kt));
+    __syncthreads();  // step kt in LDS for every lane; step kt - 1 read by every wave
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    const unsigned char* st = sm + (kt % NS) * SB;
+    bf16v8_t a[4], b[NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16v8_t*>(st + (16 * i + l16) * 64 + rs);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      b[j] = *reinterpret_cast<const bf16v8_t*>(st + AB + ((TN / 4) * wave + 16 * j + l16) * 64 + rs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     if (norm) {
-      const uint32_t v[4] = {ra.x, ra.y, ra.z, ra.w};
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + (16 * wave + l16) * 64 + rs);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const double lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xFFFF0000u);
@@ -214,34 +250,6 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
         sq += hi * hi;
       }
     }
-  };
-  f32x4_t acc[4][NJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int l16 = lane & 15, g = lane >> 4;
-  const int rslot = 8 * (g ^ ((l16 >> 2) & 3));  // rows 16 i + l16 share bits 2-3 of l16
-  const int nk = D / 32;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    bf16v8_t a[4], b[NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16v8_t*>(&As[buf][16 * i + l16][rslot]);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[j] = *reinterpret_cast<const bf16v8_t*>(&Bs[buf][(TN / 4) * wave + 16 * j + l16][rslot]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < nk) store(buf ^ 1);
-    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -253,9 +261,10 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
         if (t < T && e < E) S[(size_t)t * E + e] = acc[i][j][r];
       }
   if (norm) {
-    sq += __shfl_xor(sq, 1, 64);
-    sq += __shfl_xor(sq, 2, 64);
-    if (ak == 0 && t0 + ar < T) nx2[t0 + ar] = sq;
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    const int t = t0 + 16 * wave + l16;
+    if (g == 0 && t < T) nx2[t] = sq;
   }
 }
 
@@ -325,9 +334,9 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
   if (lane == 0) ncand[t] = base;
 }
 
-// ---- 4. exact chains of the candidates. Workgroup = 256 tokens x ERX = 96
-// experts (384 experts: 4 x 64 = 256 workgroups; a tile this large lets
-// each staged row serve several pairs). The block's candidate pairs are counted per expert and listed by
+// ---- 4. exact chains of the candidates. Workgroup = TB tokens x ERX
+// experts (a tile this large lets each staged row serve several pairs;
+// 256 x 96 from 256 experts, 64 x 32 below). The block's candidate pairs are counted per expert and listed by
 // expert (in the workspace); a unit is one expert and up to 4 of its
 // candidate tokens, so a thread runs 4 independent chains that read the
 // expert's weights once per 4 d. The x rows of the block and the W_r^T rows
@@ -336,12 +345,13 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
 // the logit). The logit and the key (logit + bias, one fp32 add) go to the
 // pair's slot in its token's candidate list. More units than threads:
 // further passes over d.
-template <int ERX>
+template <int TB, int ERX>
 __global__ __launch_bounds__(512) void screen_exact_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wt, const float* __restrict__ bias,
     const int16_t* __restrict__ cand, const int32_t* __restrict__ ncand, int T, int D, int E,
     int32_t* __restrict__ gpairs, float* __restrict__ exl, float* __restrict__ exk) {
-  constexpr int TB = kExTB, DK = kExDK, NTH = 512, UT = 4;
+  constexpr int DK = kExDK, NTH = 512, UT = 4;
+  static_assert(TB <= 256 && TB <= NTH && ERX <= NTH, "pair encoding and list build");
   constexpr int XP = DK + 8;  // bf16 row, padded to 144 bytes
   constexpr int WP = DK + 4;  // fp32 row, padded to 272 bytes
   constexpr int NXV = TB * DK / 8 / NTH;    // 16-byte x pieces per thread per chunk
@@ -615,8 +625,12 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   screen_prep_kernel<<<dim3(ceil_div(E, 32), ceil_div(D, 32)), 256, 0, s>>>(W_r, D, E, f.wt,
                                                                              f.whi, f.wmax);
   screen_norms_kernel<<<E, 256, 0, s>>>(f.wt, f.whi, D, E, f.wmax);
-  screen_gemm_kernel<128><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 128)), 256, 0, s>>>(
-      xb, f.whi, T, D, E, f.S, f.nx2);
+  if (E <= 128)  // more workgroups for few experts
+    screen_gemm_kernel<64><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 64)), 256, 0, s>>>(
+        xb, f.whi, T, D, E, f.S, f.nx2);
+  else
+    screen_gemm_kernel<128><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 128)), 256, 0, s>>>(
+        xb, f.whi, T, D, E, f.S, f.nx2);
   // 5 g_D (1 + 2^-8): the chain's own bound, the MFMA allowance and a
   // safety margin (see the derivation at the top)
   const double u = 0x1p-24, gD = D * u / (1.0 - D * u);
@@ -627,8 +641,12 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   else if (nj <= 6) screen_cand_kernel<6><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
   else if (nj <= 8) screen_cand_kernel<8><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
   else screen_cand_kernel<16><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
-  screen_exact_kernel<kExER><<<dim3(ceil_div(T, kExTB), ceil_div(E, kExER)), 512, 0, s>>>(
-      xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
+  if (E >= 256)
+    screen_exact_kernel<256, 96><<<dim3(ceil_div(T, 256), ceil_div(E, 96)), 512, 0, s>>>(
+        xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
+  else
+    screen_exact_kernel<64, 32><<<dim3(ceil_div(T, 64), ceil_div(E, 32)), 512, 0, s>>>(
+        xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
   screen_select64_kernel<<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
                                             c.gating, c.renorm, idx, w);
   screen_select_kernel<16><<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,

@@ -60,9 +60,11 @@ def test_router_instance(E, k, D, gating, renorm, act):
 
 
 SCREEN_CASES = [
-    # (E, k, D, gating, renorm); the screen runs from 256 experts, below
+    # (E, k, D, gating, renorm); the screen runs from 128 experts, below
     # that the entry point runs the exact router
+    (64, 4, 512, syn.GATE_SOFTMAX, 1),
     (128, 8, 1024, syn.GATE_SOFTMAX, 1),
+    (200, 8, 512, syn.GATE_SIGMOID, 1),
     (256, 8, 512, syn.GATE_SIGMOID, 1),
     (256, 16, 256, syn.GATE_SIGMOID, 0),
     (300, 9, 512, syn.GATE_SQRT_SOFTPLUS, 0),
