@@ -71,8 +71,8 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, const void* x, 
 
 // Builds the tile map (tilemap_ints(c) int32, M-tiles of kBM rows; with
 // `wide`, an expert's last M-tile of at most kBM / 2 rows becomes a wide
-// tile of 128 rows x 512 B-columns, which the MXFP4-weight GEMM with bf16
-// activations runs)
+// tile of 128 rows x 512 B-columns, which the MXFP4-weight GEMMs, with bf16
+// or MXFP8 activations, run)
 // from device offsets; also zeroes both banks of split flags
 // (2 kSplitSlots int32) when `flags` is not null.
 hipError_t launch_tilemap(const moe_cfg& c, const int32_t* offsets, int32_t* tilemap,
