@@ -157,7 +157,8 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
   constexpr int ASG_BYTES = SH::ASG, AS_OFF = SH::AS_OFF, COLS = SH::COLS;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform (an SGPR): the per-wave choices below become scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = WIDE ? 0 : wave >> 2;   // row half
   const int wn = WIDE ? wave : wave & 3; // column block
 
@@ -280,6 +281,15 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
   }
   // A-scale offset of absolute step t: group buffer (t / 8) % 3, 2 bytes a step
   auto as_off = [](int t) { return (uint32_t)((t / kSG) % 3 * ASG_BYTES + (t % kSG) * 2); };
+  // the same, kept step by step in the loop: t % kSG and (t / kSG) % 3
+  int t_r = kt_begin % kSG, t_g = kt_begin / kSG % 3;
+  auto ao_cur = [&]() { return (uint32_t)(t_g * ASG_BYTES + t_r * 2); };
+  auto ao_next = [&]() {
+    if (++t_r == kSG) {
+      t_r = 0;
+      t_g = t_g == 2 ? 0 : t_g + 1;
+    }
+  };
 
   // a wave whose rows all lie past the segment end keeps copying and
   // synchronising but skips its reads and MFMAs
@@ -377,17 +387,27 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
   // in flight (they complete in order): the step batches of kt + 2 ..
   // kt + NST8 - 1 and the A-scale group copies of the syncs of steps
   // kt - NST8 + 1 .. kt - 1 (each sync issues its batch, then its group copy).
+  // Every wave copies at least ACP + BCP pieces per step, so while NST8 - 2
+  // later batches are in flight, waiting down to NMIN copies is at least as
+  // strict as the exact count (a constant wait, no branches); the exact count
+  // is formed only for the last steps.
+  constexpr int NMIN = (SH::ACP + SH::BCP) * (NST8 - 2);
 #define A8_SYNC()                                                                    \
   do {                                                                               \
-    int n = per * (min(nk - 1, kt + NST8 - 1) - min(kt + 1, nk - 1));                \
-    const int lo = max(0, kt - (NST8 - 1)), hi = kt - 1;                             \
-    if (wave < SH::NAS && hi >= lo)                                                  \
-      n += ((wave - (kt_begin + lo) % kSG + kSG) % kSG) <= hi - lo;                  \
-    wait_vmcnt_dyn(n);                                                               \
+    if (kt + NST8 - 1 <= nk - 1) {                                                   \
+      wait_vmcnt<NMIN>();                                                            \
+    } else {                                                                         \
+      int n = per * (min(nk - 1, kt + NST8 - 1) - min(kt + 1, nk - 1));              \
+      const int lo = max(0, kt - (NST8 - 1)), hi = kt - 1;                           \
+      if (wave < SH::NAS && hi >= lo)                                                \
+        n += ((wave - (kt_begin + lo) % kSG + kSG) % kSG) <= hi - lo;                \
+      wait_vmcnt_dyn(n);                                                             \
+    }                                                                                \
     __builtin_amdgcn_s_barrier();                                                    \
     asm volatile("" ::: "memory");                                                   \
     if (kt + NST8 < nk) issue(kt_begin + kt + NST8, so);                             \
-    if (wave < SH::NAS && (kt_begin + kt) % kSG == wave) issue_group((kt_begin + kt) / kSG + 2); \
+    if (wave < SH::NAS && (unsigned)(kt_begin + kt) % kSG == (unsigned)wave)          \
+      issue_group((unsigned)(kt_begin + kt) / kSG + 2);                              \
   } while (0)
 
   // the first A-scale groups, then the copies of the first NST8 steps
@@ -425,12 +445,14 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
                  : "memory");
     for (; kt + 1 < nk; ++kt) {
       const uint32_t so1 = next_stage(so);
-      A8_H1(so, as_off(kt_begin + kt));
+      const uint32_t ao0 = ao_cur();
+      ao_next();
+      A8_H1(so, ao0);
       A8_SYNC();
-      A8_H2(so1, as_off(kt_begin + kt + 1));
+      A8_H2(so1, ao_cur());
       so = so1;
     }
-    A8_H1(so, as_off(kt_begin + kt));
+    A8_H1(so, ao_cur());
     A8_SYNC();
     A8_H2_LAST();
   }
