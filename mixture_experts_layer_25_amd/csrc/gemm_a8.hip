@@ -232,15 +232,25 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
     g = min(g, g_last);  // past the range: copy the last group again (same bytes)
     dma16(as_g + (size_t)g * sa_rows * 16, smem + AS_OFF + (g % 3) * ASG_BYTES + wave * 1024);
   };
+  // the steps are issued in order, each once: the sources advance a step
+  // per call
   auto issue = [&](int kt, uint32_t so) __attribute__((always_inline)) {
+    (void)kt;
     unsigned char* st = smem + so;
-    const int k = kt - kt_begin;
 #pragma unroll
-    for (int r = 0; r < SH::ACP; ++r) dma16(a_g[r] + k * BK8, st + 8192 * r + wave * 1024);
+    for (int r = 0; r < SH::ACP; ++r) {
+      dma16(a_g[r], st + 8192 * r + wave * 1024);
+      a_g[r] += BK8;
+    }
 #pragma unroll
-    for (int r = 0; r < SH::BCP; ++r)
-      dma16(bc_g[r] + k * bc_step, st + A8_BYTES + 8192 * r + wave * 1024);
-    if (wave < SH::NBS) dma4(bs_g + k * bs_step, st + A8_BYTES + B8C_BYTES + wave * 256);
+    for (int r = 0; r < SH::BCP; ++r) {
+      dma16(bc_g[r], st + A8_BYTES + 8192 * r + wave * 1024);
+      bc_g[r] += bc_step;
+    }
+    if (wave < SH::NBS) {
+      dma4(bs_g, st + A8_BYTES + B8C_BYTES + wave * 256);
+      bs_g += bs_step;
+    }
   };
   const int per = SH::ACP + SH::BCP + (wave < SH::NBS ? 1 : 0);  // this wave's copies per step
 
