@@ -337,21 +337,31 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
 #define A8_RB(OUT, ADDR, OREG, OFF, TMP)                                             \
   "v_add_u32 %[" TMP "], %[" OREG "], %[" ADDR "]\n\t"                               \
   "ds_read_u8 %[" OUT "], %[" TMP "] offset:" OFF "\n\t"
+  // A fragments of two row tiles (k-groups h and h + 2 of the lane's rows, at
+  // byte offsets O0 and O1 of the stage), the two lane addresses formed once
+#define A8_RA(O0, O1)                                                                \
+  "v_add_u32 %[u0], %[so], %[alo]\n\t"                                               \
+  "v_add_u32 %[u1], %[so], %[ahi]\n\t"                                               \
+  "ds_read_b128 %[nl0], %[u0] offset:" O0 "\n\t"                                     \
+  "ds_read_b128 %[ng0], %[u1] offset:" O0 "\n\t"                                     \
+  "ds_read_b128 %[nl1], %[u0] offset:" O1 "\n\t"                                     \
+  "ds_read_b128 %[ng1], %[u1] offset:" O1 "\n\t"
+  // their A scales (the scale ring at the A-scale offset) at O0 and O1
+#define A8_RS(O0, O1)                                                                \
+  "v_add_u32 %[u0], %[ao], %[as]\n\t"                                                \
+  "ds_read_u8 %[ns0], %[u0] offset:" O0 "\n\t"                                       \
+  "ds_read_u8 %[ns1], %[u0] offset:" O1 "\n\t"
   // first half: this step's second B fragment and its scale (b1, t1: the
   // oldest reads, needed by the third MFMA), then Q of this step (A rows
   // 64.., their scales 1024..)
 #define A8_RQ                                                                        \
   A8_R("b1", "bc1", "0", "u0") A8_RB("t1", "bs1", "so", "0", "u1"),                  \
-      A8_R("nl0", "alo", "4096", "u0") A8_R("ng0", "ahi", "4096", "u1")              \
-      A8_R("nl1", "alo", "6144", "u0") A8_R("ng1", "ahi", "6144", "u1")              \
-      A8_RB("ns0", "as", "ao", "1024", "u0") A8_RB("ns1", "as", "ao", "1536", "u1"),  \
+      A8_RA("4096", "6144") A8_RS("1024", "1536"),                                   \
       "s_waitcnt lgkmcnt(6)\n\t", "", ""
   // second half: P of the next step, then (after the last use of b0) its
   // first B fragment and scale; its b1, t1 are read by its first half
 #define A8_RP                                                                        \
-  "", A8_R("nl0", "alo", "0", "u0") A8_R("ng0", "ahi", "0", "u1")                    \
-      A8_R("nl1", "alo", "2048", "u0") A8_R("ng1", "ahi", "2048", "u1")              \
-      A8_RB("ns0", "as", "ao", "0", "u0") A8_RB("ns1", "as", "ao", "512", "u1"),     \
+  "", A8_RA("0", "2048") A8_RS("0", "512"),                                          \
       A8_R("b0", "bc0", "0", "u0") A8_RB("t0", "bs0", "so", "0", "u1"), "", ""
 #define A8_BASES                                                                     \
   [alo] "v"(a_lo), [ahi] "v"(a_hi), [bc0] "v"(bc_a[0]), [bc1] "v"(bc_a[1]),          \
@@ -476,6 +486,8 @@ __device__ __forceinline__ void gemm_a8_body(const Args& a, const Job& jb, unsig
 #undef A8_BASES
 #undef A8_RP
 #undef A8_RQ
+#undef A8_RS
+#undef A8_RA
 #undef A8_RB
 #undef A8_R
 #undef A8_HALF_X
