@@ -182,9 +182,9 @@ __global__ __launch_bounds__(256) void screen_norms_kernel(const float* __restri
 // that the 16 lanes of a fragment read, rows r..r+15 of one k-group, hit 16
 // distinct 16-byte bank groups. Lane l supplies row l%16 of A and column
 // l%16 of B with k = 8 (l/16) .. +7 and holds rows 4 (l/16) + r of column
-// l%16 of the 16 x 16 result. The workgroups of the first expert tile also
-// sum x_t^2 in double: wave w over rows 16 w .. 16 w + 15 of its A
-// fragments, then the 4 lanes of a row.
+// l%16 of the 16 x 16 result. The token tile's workgroups also sum x_t^2 in
+// double: wave w of expert tile w mod (expert tiles) over rows 16 w ..
+// 16 w + 15 of its A fragments, then the 4 lanes of a row.
 template <int TN>
 __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ whi,
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
   constexpr int PER = 1 + TN / 64;             // 16-byte copies per thread per step
   constexpr int NJ = TN / 64;                  // 16-column MFMA tiles per wave
   __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * SB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * kScrTM, e0 = blockIdx.y * TN;
   // the copies: this lane's row of A (and of each W^T quarter) and k-group
   const int cr = 16 * wave + (lane >> 2), cs = lane & 3;
@@ -214,7 +214,9 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int q = 0; q < NJ; ++q) dma16(bg[q] + 32 * kt, st + AB + 4096 * q + 1024 * wave);
   };
-  const bool norm = blockIdx.y == 0;
+  // wave w's 16 rows are summed by the expert tile w mod gridDim.y, so the
+  // double-precision squares are spread over the token tile's workgroups
+  const bool norm = (int)(wave % gridDim.y) == (int)blockIdx.y;
   double sq = 0.0;
   f32x4_t acc[4][NJ];
 #pragma unroll
