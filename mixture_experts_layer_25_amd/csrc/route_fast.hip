@@ -28,7 +28,8 @@
 // w_de| with g_D = D u / (1 - D u), u = 2^-24. The screen's products are
 // exact; its accumulation error is bounded here by twice the same bound
 // (an allowance for truncating or reordered accumulation inside the MFMA,
-// whose summation order is not specified) and once more for safety, and the
+// whose summation order is not specified; a k-split into two halves of D
+// added in fp32 is one more such order) and once more for safety, and the
 // bf16 residual adds |sum_d x_d (h_de - w_de)| <= ||x_t|| ||r_e||. With
 // sum |x_d w_de| <= ||x_t|| ||w_e|| and |h| <= (1 + 2^-8) |w|:
 //   |a_e - c_e| <= eps_t = ||x_t|| (R + 5 g_D (1 + 2^-8) N),
@@ -76,6 +77,14 @@ struct ScreenWs {
   size_t bytes;
 };
 
+// k-split of the screen GEMM: two halves of D (summed in order by the
+// candidate kernel) when its tiles alone would give under two workgroups
+// per CU
+int screen_ksplit(const moe_cfg& c) {
+  const long long tiles = (long long)ceil_div(c.T, kScrTM) * ceil_div(c.E, c.E <= 128 ? 64 : 128);
+  return tiles < 512 && c.D >= 64 * 32 ? 2 : 1;
+}
+
 ScreenWs carve(const moe_cfg& c, void* base) {
   char* p = static_cast<char*>(base);
   size_t off = 0;
@@ -90,8 +99,9 @@ ScreenWs carve(const moe_cfg& c, void* base) {
   w.whi = reinterpret_cast<uint16_t*>(take(ED * 2));
   w.wt = reinterpret_cast<float*>(take(ED * 4));
   w.wmax = reinterpret_cast<unsigned long long*>(take(16));
-  w.S = reinterpret_cast<float*>(take(TE * 4));
-  w.nx2 = reinterpret_cast<double*>(take((size_t)c.T * 8));
+  const int ks = screen_ksplit(c);
+  w.S = reinterpret_cast<float*>(take(ks * TE * 4));
+  w.nx2 = reinterpret_cast<double*>(take((size_t)ks * c.T * 8));
   w.cand = reinterpret_cast<int16_t*>(take(TE * 2));
   w.ncand = reinterpret_cast<int32_t*>(take((size_t)c.T * 4));
   w.exl = reinterpret_cast<float*>(take(TE * 4));
@@ -198,16 +208,22 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * kScrTM, e0 = blockIdx.y * TN;
+  // k-split z = blockIdx.z of gridDim.z: steps [k0, k0 + nk) of the D / 32,
+  // partial sums to S and nx2 slice z
+  const int nkd = D / 32, per = (nkd + gridDim.z - 1) / gridDim.z;
+  const int k0 = blockIdx.z * per, nk = min(nkd, k0 + per) - k0;
+  S += (size_t)blockIdx.z * T * E;
+  nx2 += (size_t)blockIdx.z * T;
   // the copies: this lane's row of A (and of each W^T quarter) and k-group
   const int cr = 16 * wave + (lane >> 2), cs = lane & 3;
-  const uint16_t* ag = x + (size_t)min(t0 + cr, T - 1) * D + 8 * (cs ^ ((cr >> 2) & 3));
+  const uint16_t* ag =
+      x + (size_t)min(t0 + cr, T - 1) * D + 32 * k0 + 8 * (cs ^ ((cr >> 2) & 3));
   const uint16_t* bg[NJ];
 #pragma unroll
   for (int q = 0; q < NJ; ++q) {
     const int r = 64 * q + cr;
-    bg[q] = whi + (size_t)min(e0 + r, E - 1) * D + 8 * (cs ^ ((r >> 2) & 3));
+    bg[q] = whi + (size_t)min(e0 + r, E - 1) * D + 32 * k0 + 8 * (cs ^ ((r >> 2) & 3));
   }
-  const int nk = D / 32;
   auto issue = [&](int kt) __attribute__((always_inline)) {
     unsigned char* st = sm + (kt % NS) * SB;
     dma16(ag + 32 * kt, st + 1024 * wave);
@@ -277,7 +293,7 @@ __global__ __launch_bounds__(256) void screen_gemm_kernel(const uint16_t* __rest
 template <int NJ>
 __global__ __launch_bounds__(256) void screen_cand_kernel(
     const float* __restrict__ S, const double* __restrict__ nx2, const float* __restrict__ bias,
-    const unsigned long long* __restrict__ wmax, double cg, int T, int E, int k,
+    const unsigned long long* __restrict__ wmax, double cg, int ks, int T, int E, int k,
     int16_t* __restrict__ cand, int32_t* __restrict__ ncand) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -290,10 +306,16 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     avail[j] = j < nj && e < E;
-    ka[j] = avail[j] ? S[(size_t)t * E + e] + (bias ? bias[e] : 0.0f) : -INFINITY;
+    float a = 0.0f;
+    if (avail[j]) {
+      a = S[(size_t)t * E + e];
+      for (int z = 1; z < ks; ++z) a += S[((size_t)z * T + t) * E + e];  // k-split parts in order
+    }
+    ka[j] = avail[j] ? a + (bias ? bias[e] : 0.0f) : -INFINITY;
     if (avail[j]) amax = fmaxf(amax, fabsf(ka[j]));
   }
-  const double nxt = nx2[t];
+  double nxt = nx2[t];
+  for (int z = 1; z < ks; ++z) nxt += nx2[(size_t)z * T + t];
   const double N = __longlong_as_double((long long)wmax[0]);
   const double R = __longlong_as_double((long long)wmax[1]);
   // the k-th largest approximate key: the largest order-preserving code U
@@ -627,11 +649,12 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   screen_prep_kernel<<<dim3(ceil_div(E, 32), ceil_div(D, 32)), 256, 0, s>>>(W_r, D, E, f.wt,
                                                                              f.whi, f.wmax);
   screen_norms_kernel<<<E, 256, 0, s>>>(f.wt, f.whi, D, E, f.wmax);
+  const int ks = screen_ksplit(c);
   if (E <= 128)  // more workgroups for few experts
-    screen_gemm_kernel<64><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 64)), 256, 0, s>>>(
+    screen_gemm_kernel<64><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 64), ks), 256, 0, s>>>(
         xb, f.whi, T, D, E, f.S, f.nx2);
   else
-    screen_gemm_kernel<128><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 128)), 256, 0, s>>>(
+    screen_gemm_kernel<128><<<dim3(ceil_div(T, kScrTM), ceil_div(E, 128), ks), 256, 0, s>>>(
         xb, f.whi, T, D, E, f.S, f.nx2);
   // 5 g_D (1 + 2^-8): the chain's own bound, the MFMA allowance and a
   // safety margin (see the derivation at the top)
@@ -639,10 +662,10 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   const double cg = 5.0 * gD * (1.0 + 0x1p-8);
   const int nj = ceil_div(E, 64);
   const dim3 g4(ceil_div(T, 4));
-  if (nj <= 4) screen_cand_kernel<4><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
-  else if (nj <= 6) screen_cand_kernel<6><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
-  else if (nj <= 8) screen_cand_kernel<8><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
-  else screen_cand_kernel<16><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, T, E, c.top_k, f.cand, f.ncand);
+  if (nj <= 4) screen_cand_kernel<4><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, ks, T, E, c.top_k, f.cand, f.ncand);
+  else if (nj <= 6) screen_cand_kernel<6><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, ks, T, E, c.top_k, f.cand, f.ncand);
+  else if (nj <= 8) screen_cand_kernel<8><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, ks, T, E, c.top_k, f.cand, f.ncand);
+  else screen_cand_kernel<16><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, ks, T, E, c.top_k, f.cand, f.ncand);
   if (E >= 256)
     screen_exact_kernel<256, 96><<<dim3(ceil_div(T, 256), ceil_div(E, 96)), 512, 0, s>>>(
         xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
