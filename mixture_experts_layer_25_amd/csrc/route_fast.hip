@@ -42,6 +42,9 @@
 // threshold is compared in double. Inputs are assumed finite.
 #include <math.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "gating.h"
 #include "gemm_tile.h"
@@ -358,23 +361,42 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
   if (lane == 0) ncand[t] = base;
 }
 
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+template <class F, int... S>
+__device__ __forceinline__ void for_each_index_(F&& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void for_each_index(F&& f) {
+  for_each_index_(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---- 4. exact chains of the candidates. Workgroup = TB tokens x ERX
 // experts (a tile this large lets each staged row serve several pairs;
-// 256 x 96 from 256 experts, 64 x 32 below). The block's candidate pairs are counted per expert and listed by
-// expert (in the workspace); a unit is one expert and up to 4 of its
-// candidate tokens, so a thread runs 4 independent chains that read the
-// expert's weights once per 4 d. The x rows of the block and the W_r^T rows
-// of the expert range stream through LDS in chunks of 64 d; each chain runs
-// d ascending from +0, one fused multiply-add per term (the definition of
-// the logit). The logit and the key (logit + bias, one fp32 add) go to the
-// pair's slot in its token's candidate list. More units than threads:
-// further passes over d.
-template <int TB, int ERX>
+// 256 x 96 from 256 experts, 64 x 32 below). The block's candidate pairs
+// are counted per expert and listed by expert (in the workspace); a unit is
+// one expert and up to UT of its candidate tokens, so a thread runs UT
+// independent chains that read the expert's weights once per 4 d. The x
+// rows of the block and the W_r^T rows of the expert range stream through
+// LDS in chunks of 64 d; each chain runs d ascending from +0, one fused
+// multiply-add per term (the definition of the logit). The logit and the
+// key (logit + bias, one fp32 add) go to the pair's slot in its token's
+// candidate list. More units than threads: further passes over d.
+//
+// The time goes to the chains themselves (a variant without them runs in
+// 14-22 us of the 75-155), i.e. to the longest run of chain steps on one
+// SIMD: UT chains per lane, each a conversion and an FMA per term. The
+// small tiles (about 190 pairs on the 128-expert layer) run one chain per
+// unit (UT = 1) in three busy waves; the large ones (about 670 pairs on
+// the 384-expert layer) three per unit, with units dealt round-robin to
+// waves 0..3 (BAL) so that all four SIMDs carry about 56 lanes of 3 chains
+// rather than three SIMDs 64 lanes of 4 (136 against 155 us).
+template <int TB, int ERX, int UT, int PF, bool BAL>
 __global__ __launch_bounds__(512) void screen_exact_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wt, const float* __restrict__ bias,
     const int16_t* __restrict__ cand, const int32_t* __restrict__ ncand, int T, int D, int E,
     int32_t* __restrict__ gpairs, float* __restrict__ exl, float* __restrict__ exk) {
-  constexpr int DK = kExDK, NTH = 512, UT = 4;
+  constexpr int DK = kExDK, NTH = 512;
   static_assert(TB <= 256 && TB <= NTH && ERX <= NTH, "pair encoding and list build");
   constexpr int XP = DK + 8;  // bf16 row, padded to 144 bytes
   constexpr int WP = DK + 4;  // fp32 row, padded to 272 bytes
@@ -424,39 +446,51 @@ __global__ __launch_bounds__(512) void screen_exact_kernel(
   const int nunits = ucum[ERX];
   if (nunits == 0) return;
 
-  // ---- chunk staging (registers -> LDS, double-buffered)
-  uint4 rx[NXV], rw[NWV];
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
-    const int d0 = c * DK;
+  // ---- chunk staging: global -> registers -> LDS. The LDS holds two
+  // chunks (the one being read and the next); the registers hold the next
+  // PF chunks, whose loads are issued PF chunks ahead so that the latency
+  // of a load from L2 or memory (1-2 us) spreads over PF chunks of chains.
+  // Every step issues the same loads, unconditionally: chunk indices past
+  // the end, d past D (the second half of a last 32-d chunk) and tokens or
+  // experts past the tile's end are clamped to valid addresses and their
+  // data is never read, so the compiler's wait before a chunk's LDS store
+  // counts only the PF - 1 younger chunks, never all of them.
+  const int nch = (D + DK - 1) / DK;
+  u32x4_t rx[PF][NXV], rw[PF][NWV];  // native vectors: kept in registers
+  auto load_chunk = [&](int c, u32x4_t(&qx)[NXV], u32x4_t(&qw)[NWV]) __attribute__((always_inline)) {
+    const int d0 = min(c, nch - 1) * DK;
 #pragma unroll
     for (int i = 0; i < NXV; ++i) {
       const int v = tid + NTH * i, tl = v / (DK / 8), dg = v % (DK / 8);
       const int t = min(t0 + tl, T - 1), d = d0 + 8 * dg;
-      rx[i] = d < D ? *reinterpret_cast<const uint4*>(x + (size_t)t * D + d) : make_uint4(0, 0, 0, 0);
+      qx[i] = *reinterpret_cast<const u32x4_t*>(x + (size_t)t * D + min(d, D - 8));
     }
 #pragma unroll
     for (int i = 0; i < NWV; ++i) {
       const int v = tid + NTH * i, el = v / (DK / 4), dg = v % (DK / 4);
       const int e = min(e0 + el, E - 1), d = d0 + 4 * dg;
-      rw[i] = d < D ? *reinterpret_cast<const uint4*>(wt + (size_t)e * D + d) : make_uint4(0, 0, 0, 0);
+      qw[i] = *reinterpret_cast<const u32x4_t*>(wt + (size_t)e * D + min(d, D - 4));
     }
   };
-  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
+  auto store_chunk = [&](int buf, const u32x4_t(&qx)[NXV], const u32x4_t(&qw)[NWV])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NXV; ++i) {
       const int v = tid + NTH * i, tl = v / (DK / 8), dg = v % (DK / 8);
-      *reinterpret_cast<uint4*>(&xs[buf][tl][8 * dg]) = rx[i];
+      *reinterpret_cast<u32x4_t*>(&xs[buf][tl][8 * dg]) = qx[i];
     }
 #pragma unroll
     for (int i = 0; i < NWV; ++i) {
       const int v = tid + NTH * i, el = v / (DK / 4), dg = v % (DK / 4);
-      *reinterpret_cast<uint4*>(&ws[buf][el][4 * dg]) = rw[i];
+      *reinterpret_cast<u32x4_t*>(&ws[buf][el][4 * dg]) = qw[i];
     }
   };
 
-  const int nch = (D + DK - 1) / DK;
   for (int u0 = 0; u0 < nunits; u0 += NTH) {
-    const int un = u0 + tid;
+    // units u0 .. u0 + 255 go round-robin to waves 0..3 (one per SIMD),
+    // the next 256 to waves 4..7
+    const int wv = tid >> 6;
+    const int un = BAL ? u0 + (wv >> 2) * 256 + (tid & 63) * 4 + (wv & 3) : u0 + tid;
     const bool mine = un < nunits;
     // the unit's expert: the last el with ucum[el] <= un
     int el = 0;
@@ -481,31 +515,44 @@ __global__ __launch_bounds__(512) void screen_exact_kernel(
     float acc[UT];
 #pragma unroll
     for (int i = 0; i < UT; ++i) acc[i] = 0.0f;
-    load_chunk(0);
-    store_chunk(0);
+    // chunk c sits in register slot c % PF until it is stored to LDS; the
+    // slots are named by compile-time indices (unrolled through
+    // for_each_index) so that they stay in registers
+    for_each_index<PF>([&](auto si) __attribute__((always_inline)) {
+      constexpr int s = decltype(si)::value;
+      load_chunk(s, rx[s], rw[s]);
+    });
+    store_chunk(0, rx[0], rw[0]);
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < nch) load_chunk(c + 1);
-      if (mine) {
-        const float* wr = &ws[buf][el][0];
-        auto step = [&](int dd) __attribute__((always_inline)) {
-          const float4 wv = *reinterpret_cast<const float4*>(wr + dd);
+    for (int cb = 0; cb < nch; cb += PF) {
+      for_each_index<PF>([&](auto si) __attribute__((always_inline)) {
+        constexpr int s = decltype(si)::value;
+        const int c = cb + s;
+        // slot s (chunk c) went to LDS before this step: refill it
+        load_chunk(c + PF, rx[s], rw[s]);
+        if (c < nch) {
+          const int buf = c & 1;
+          if (mine) {
+            const float* wr = &ws[buf][el][0];
+            auto step = [&](int dd) __attribute__((always_inline)) {
+              const float4 wv = *reinterpret_cast<const float4*>(wr + dd);
 #pragma unroll
-          for (int i = 0; i < UT; ++i) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(&xs[buf][tl[i]][dd]);
-            acc[i] = __builtin_fmaf(__uint_as_float(xv.x << 16), wv.x, acc[i]);
-            acc[i] = __builtin_fmaf(__uint_as_float(xv.x & 0xFFFF0000u), wv.y, acc[i]);
-            acc[i] = __builtin_fmaf(__uint_as_float(xv.y << 16), wv.z, acc[i]);
-            acc[i] = __builtin_fmaf(__uint_as_float(xv.y & 0xFFFF0000u), wv.w, acc[i]);
-          }
-        };
-        const int dk = min(DK, D - c * DK);  // 64, or 32 for a last chunk
+              for (int i = 0; i < UT; ++i) {
+                const uint2 xv = *reinterpret_cast<const uint2*>(&xs[buf][tl[i]][dd]);
+                acc[i] = __builtin_fmaf(__uint_as_float(xv.x << 16), wv.x, acc[i]);
+                acc[i] = __builtin_fmaf(__uint_as_float(xv.x & 0xFFFF0000u), wv.y, acc[i]);
+                acc[i] = __builtin_fmaf(__uint_as_float(xv.y << 16), wv.z, acc[i]);
+                acc[i] = __builtin_fmaf(__uint_as_float(xv.y & 0xFFFF0000u), wv.w, acc[i]);
+              }
+            };
+            const int dk = min(DK, D - c * DK);  // 64, or 32 for a last chunk
 #pragma unroll 4
-        for (int dd = 0; dd < dk; dd += 4) step(dd);
-      }
-      if (c + 1 < nch) store_chunk(buf ^ 1);
-      __syncthreads();
+            for (int dd = 0; dd < dk; dd += 4) step(dd);
+          }
+          if (c + 1 < nch) store_chunk(buf ^ 1, rx[(s + 1) % PF], rw[(s + 1) % PF]);
+          __syncthreads();
+        }
+      });
     }
     const float b = bias ? bias[e0 + el] : 0.0f;
 #pragma unroll
@@ -667,11 +714,13 @@ hipError_t launch_router_screened(const moe_cfg& c, const void* x, const float* 
   else if (nj <= 8) screen_cand_kernel<8><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, ks, T, E, c.top_k, f.cand, f.ncand);
   else screen_cand_kernel<16><<<g4, 256, 0, s>>>(f.S, f.nx2, bias, f.wmax, cg, ks, T, E, c.top_k, f.cand, f.ncand);
   if (E >= 256)
-    screen_exact_kernel<256, 96><<<dim3(ceil_div(T, 256), ceil_div(E, 96)), 512, 0, s>>>(
-        xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
+    screen_exact_kernel<256, 96, 3, 2, true>
+        <<<dim3(ceil_div(T, 256), ceil_div(E, 96)), 512, 0, s>>>(xb, f.wt, bias, f.cand, f.ncand,
+                                                                  T, D, E, f.gpairs, f.exl, f.exk);
   else
-    screen_exact_kernel<64, 32><<<dim3(ceil_div(T, 64), ceil_div(E, 32)), 512, 0, s>>>(
-        xb, f.wt, bias, f.cand, f.ncand, T, D, E, f.gpairs, f.exl, f.exk);
+    screen_exact_kernel<64, 32, 1, 2, false>
+        <<<dim3(ceil_div(T, 64), ceil_div(E, 32)), 512, 0, s>>>(xb, f.wt, bias, f.cand, f.ncand,
+                                                                 T, D, E, f.gpairs, f.exl, f.exk);
   screen_select64_kernel<<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
                                             c.gating, c.renorm, idx, w);
   screen_select_kernel<16><<<g4, 256, 0, s>>>(f.cand, f.ncand, f.exl, f.exk, T, E, c.top_k,
