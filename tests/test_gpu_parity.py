@@ -33,6 +33,10 @@ SMALL = {
     # above 128 rows, and wide last M-tiles of 65..128 and of at most 64 rows
     "mxfp4_mixed_tiles": syn.small_variant(syn.CONFIGS["fine384_mxfp4"], T=600, D=256, F=160,
                                            E=16, shared_F=96),
+    # fp32 layer over several 64 x 64 tiles of the fp32 MFMA GEMM: segments
+    # of 2-3 M-tiles with ragged last tiles, F and D not multiples of 64,
+    # K = D not a multiple of the 16-deep LDS step
+    "fp32_tiles": syn.small_variant(syn.CONFIGS["tiny_fp32"], T=300, D=136, F=200),
 }
 
 
@@ -81,7 +85,7 @@ def test_small_fused_equals_stagewise(name):
     assert np.array_equal(b["y"], c["y"]), "two runs differ (must be deterministic)"
 
 
-@pytest.mark.parametrize("name", [n for n in SMALL if n != "tiny_fp32"])
+@pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].act != syn.F32])
 def test_small_gathered_gate_up_equals_dispatched(name):
     """moe_expert_gate_up_gathered (rows read from x through perm_token, after
     a dispatch that copies no rows) writes the same H, byte for byte, as
