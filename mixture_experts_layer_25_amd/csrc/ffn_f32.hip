@@ -66,7 +66,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
 }
 
 // ---- fp32 grouped GEMM on v_mfma_f32_16x16x4_f32. A tile is 64 rows of
-// one expert's segment x 64 columns; K streams through LDS in steps of 16
+// one expert's segment x 64 columns; K streams through LDS in steps of 32
 // (the next step's operands are loaded into registers while the current
 // one is multiplied). Workgroup = 4 waves, wave w owns rows 32 (w / 2) ..
 // and columns 32 (w % 2) .. of the tile as 2 x 2 blocks of 16 x 16. M-tile
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
 // epilogue forms h = SiLU(clamp(g)) * clamp(u) in fp32; DOWN: one matrix,
 // fp32 out. The MFMA's summation order is its own; fp32 products and
 // accumulation keep the result within the fp32 layer's tolerance.
-constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 32;
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
@@ -122,28 +122,37 @@ __global__ __launch_bounds__(256) void ffn_f32_gemm_kernel(
   const float* Bw0 = B0 + (size_t)e * K * N;
   const float* Bw1 = SWIGLU ? B1 + (size_t)e * K * N : nullptr;
 
-  // ---- operand loads: thread -> one float4 of A (row tid / 4, k 4 (tid % 4))
-  // and one of each B (k tid / 16, columns 4 (tid % 16)); zero outside
-  const int ar = tid >> 2, ak = 4 * (tid & 3);
-  const int bk = tid >> 4, bn = 4 * (tid & 15);
-  const bool a_row_ok = row0 + ar < row_end;
+  // ---- operand loads: thread -> float4 p of A (row (tid + 256 p) / 8,
+  // k 4 (tid % 8)) and of each B (k (tid + 256 p) / 16, columns 4 (tid % 16)),
+  // p = 0, 1; zero outside the tile's rows, N and K
+  constexpr int NP = BK / 16;  // float4 pieces per thread and operand
+  static_assert(BM * BK == 4 * 256 * NP && BK * BN == 4 * 256 * NP, "load shape");
+  const int ak = 4 * (tid % (BK / 4)), bn = 4 * (tid & 15);
   const bool b_col_ok = n0 + bn < N;  // N % 4 == 0: a float4 is wholly in or out
-  f32x4v_t ra, rb[NB];
+  f32x4v_t ra[NP], rb[NB][NP];
   auto load = [&](int k0) __attribute__((always_inline)) {
     const f32x4v_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-    ra = a_row_ok && k0 + ak < K
-             ? *reinterpret_cast<const f32x4v_t*>(A + (size_t)(row0 + ar) * K + k0 + ak)
-             : z;
-    const bool bok = b_col_ok && k0 + bk < K;
-    rb[0] = bok ? *reinterpret_cast<const f32x4v_t*>(Bw0 + (size_t)(k0 + bk) * N + n0 + bn) : z;
-    if constexpr (SWIGLU)
-      rb[1] = bok ? *reinterpret_cast<const f32x4v_t*>(Bw1 + (size_t)(k0 + bk) * N + n0 + bn) : z;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int ar = (tid + 256 * p) / (BK / 4), bk = (tid + 256 * p) >> 4;
+      ra[p] = row0 + ar < row_end && k0 + ak < K
+                  ? *reinterpret_cast<const f32x4v_t*>(A + (size_t)(row0 + ar) * K + k0 + ak)
+                  : z;
+      const bool bok = b_col_ok && k0 + bk < K;
+      rb[0][p] = bok ? *reinterpret_cast<const f32x4v_t*>(Bw0 + (size_t)(k0 + bk) * N + n0 + bn) : z;
+      if constexpr (SWIGLU)
+        rb[1][p] = bok ? *reinterpret_cast<const f32x4v_t*>(Bw1 + (size_t)(k0 + bk) * N + n0 + bn) : z;
+    }
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) As[ak + i][ar] = ra[i];
+    for (int p = 0; p < NP; ++p) {
+      const int ar = (tid + 256 * p) / (BK / 4), bk = (tid + 256 * p) >> 4;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4v_t*>(&Bs[b][bk][bn]) = rb[b];
+      for (int i = 0; i < 4; ++i) As[ak + i][ar] = ra[p][i];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4v_t*>(&Bs[b][bk][bn]) = rb[b][p];
+    }
   };
 
   f32x4v_t acc[NB][2][2];
