@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
-PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 (vector and MFMA)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
 
 
@@ -89,8 +89,9 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc")
 def roofline_kernel(cfg):
     """The gate/up kernel the workload's weight type selects, its source
     file and what bounds it."""
-    if cfg.wdt == 0:
-        return {"name": "ffn_f32_gateup_kernel", "src": "ffn_f32.hip", "bound": "alu"}
+    if cfg.wdt == 0:  # fp32 MFMA: the same 157.3 TFLOP/s as the fp32 vector ALUs
+        return {"name": "ffn_f32_gemm_kernel<true>", "src": "ffn_f32.hip", "bound": "mfma",
+                "peak": PEAK_FP32_TFLOPS}
     if cfg.wdt == 3:  # e4m3 x e2m1 products run at the fp8 MFMA rate
         return {"name": "gemm_a8_kernel<0>", "src": "gemm_a8.hip", "bound": "mfma",
                 "peak": PEAK_FP8_TFLOPS}
@@ -187,8 +188,9 @@ def summarize_trace(run_dir, workload, command):
 
 
 # MFMA flops per busy pipe cycle and SIMD: v_mfma_f32_16x16x32_bf16 (16384
-# flops in 16 cycles) and the block-scaled fp8 x fp4 MFMA (twice the rate)
-MFMA_FLOP_PER_CYCLE = {"gemm16": 1024, "gemm_a8": 2048}
+# flops in 16 cycles), the block-scaled fp8 x fp4 MFMA (twice the rate) and
+# v_mfma_f32_16x16x4_f32 (2048 flops in 32 cycles)
+MFMA_FLOP_PER_CYCLE = {"gemm16": 1024, "gemm_a8": 2048, "ffn_f32_gemm": 64}
 XCDS = 8
 
 
