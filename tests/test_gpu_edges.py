@@ -105,6 +105,15 @@ def test_sigmoid_renorm_fp32():
     _run(cfg)
 
 
+def test_fp32_clamp_multi_tile():
+    """fp32 MFMA GEMM with an active clamp on gate and up (|pre-activation|
+    has sigma about 0.02 sqrt(D) = 0.3, so a bound of 0.2 clamps a large share
+    of them) over segments of several 64-row tiles."""
+    cfg = syn.Config("clampfp32", T=400, D=240, E=4, k=2, F=104, act=syn.F32, wdt=syn.F32,
+                     gating=syn.GATE_SOFTMAX, renorm=1, clamp=0.2)
+    _run(cfg)
+
+
 def test_zero_tokens():
     cfg = upload.cfg_of(BASE.replace(T=0))
     dev = torch.device("cuda")
