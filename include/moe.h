@@ -8,7 +8,11 @@
  * moe_set_split_wait). Every call validates its arguments on the
  * host and then only enqueues kernels on `stream` (a hipStream_t passed as
  * void*; NULL means the default stream); results are ready once the stream
- * reaches that point. No C++ exception crosses this boundary.
+ * reaches that point. Nothing but kernel launches reaches the stream (the
+ * split GEMMs' ready flags are cleared by a kernel, not a memset), so a call
+ * may be captured into a HIP graph; each replay recomputes everything from
+ * the buffers' contents at replay time. No C++ exception crosses this
+ * boundary.
  *
  * Layer (sources cited by page title and section):
  *   y[t] = sum_{j < k, kept} w[t][j] * SwiGLU_{e(t,j)}(x[t]) + shared(x[t])
