@@ -190,7 +190,8 @@ int moe_route_screened(const moe_cfg* cfg, const void* x, const float* W_r, cons
  * MOE_MXFP4_A8: the row's MXFP8 quantisation, quantised once per token).
  * x_perm may be NULL: then no row is copied (for callers that gather the
  * rows through perm_token, as moe_expert_gate_up_gathered does).
- * Integer outputs are deterministic and bit-exact. */
+ * Integer outputs are deterministic and bit-exact. T = 0: counts and
+ * offsets are written as zeros and nothing else is enqueued. */
 int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
                  int32_t* offsets, int32_t* slot_pos, int32_t* perm_token, void* x_perm,
                  void* ws, size_t ws_bytes, void* stream);
@@ -260,7 +261,8 @@ int moe_combine(const moe_cfg* cfg, const float* y_perm, const int32_t* slot_pos
  * outputs (NULL: kept in the workspace). With bf16 activations the gate/up
  * GEMM fetches each routed row from x through perm_token, so the
  * dispatched copy x_perm is never written; the results are the same as
- * those of the stage entry points. */
+ * those of the stage entry points. T = 0: the optional counts and offsets
+ * are written as zeros and nothing else is enqueued. */
 int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float* bias,
                 const moe_weights* w, void* y, int32_t* topk_idx, float* topk_w,
                 int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream);

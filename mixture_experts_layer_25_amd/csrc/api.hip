@@ -346,7 +346,9 @@ int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int
       !dev_ok(slot_pos) || !dev_ok(perm_token) || !opt_ok(x_perm))
     return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws) || ws_bytes < dispatch_ws(*cfg)) return MOE_ERR_WORKSPACE;
-  if (cfg->T == 0) return MOE_OK;
+  if (cfg->T == 0)
+    return hip_status(moe::launch_dispatch_empty(*cfg, counts, offsets,
+                                                 static_cast<hipStream_t>(stream)));
   return hip_status(moe::launch_dispatch(*cfg, topk_idx, x, counts, offsets, slot_pos, perm_token,
                                          x_perm, static_cast<int32_t*>(ws),
                                          static_cast<hipStream_t>(stream)));
@@ -362,7 +364,9 @@ int moe_dispatch_noalloc(const moe_cfg* cfg, const int32_t* topk_idx, const void
     return MOE_ERR_INVALID_ARG;
   if ((size_t)cfg->E * moe::num_chunks(*cfg) > moe::kDispatchScratchInts)
     return MOE_ERR_SCRATCH;
-  if (cfg->T == 0) return MOE_OK;
+  if (cfg->T == 0)
+    return hip_status(moe::launch_dispatch_empty(*cfg, counts, offsets,
+                                                 static_cast<hipStream_t>(stream)));
   int32_t* scratch = nullptr;
   hipError_t e = moe::dispatch_scratch(&scratch);
   if (e != hipSuccess) return hip_status(e);
@@ -469,7 +473,9 @@ int moe_forward(const moe_cfg* cfg, const void* x, const float* W_r, const float
     return MOE_ERR_INVALID_ARG;
   const ForwardWs f0 = carve_forward(*cfg, nullptr);
   if (!ws || !aligned16(ws) || ws_bytes < f0.bytes) return MOE_ERR_WORKSPACE;
-  if (cfg->T == 0) return MOE_OK;
+  if (cfg->T == 0)  // y has no rows; the optional counts and offsets are zero
+    return hip_status(moe::launch_dispatch_empty(*cfg, counts, offsets,
+                                                 static_cast<hipStream_t>(stream)));
   const moe_cfg& c = *cfg;
   const ForwardWs f = carve_forward(c, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);

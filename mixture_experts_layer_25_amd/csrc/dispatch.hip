@@ -238,7 +238,24 @@ __global__ __launch_bounds__(256) void dispatch_copy_mxfp8_kernel(
   }
 }
 
+// T = 0: no pair to dispatch; the counts and offsets of the empty layer
+// (a kernel, not a memset, so that the call stays capturable into a graph)
+__global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  for (int e = blockIdx.x * 256 + threadIdx.x; e <= E; e += gridDim.x * 256) {
+    if (counts && e < E) counts[e] = 0;
+    if (offsets) offsets[e] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dispatch_empty(const moe_cfg& c, int32_t* counts, int32_t* offsets,
+                                 hipStream_t s) {
+  if (!counts && !offsets) return hipSuccess;
+  dispatch_empty_kernel<<<ceil_div(c.E + 1, 256), 256, 0, s>>>(c.E, counts, offsets);
+  return hipGetLastError();
+}
 
 // Scratch of the no-allocation dispatch (moe_dispatch_noalloc): the
 // per-chunk expert counts, int32 [E][ceil(T/256)], at most

@@ -199,7 +199,8 @@ def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None, copy_rows=True):
     tk = cfg.T * cfg.top_k
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
     offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
-    slot_pos = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+    # at least one row, so that no pointer is null at T = 0
+    slot_pos = torch.empty((max(cfg.T, 1), cfg.top_k), dtype=torch.int32, device=dev)
     perm = torch.full((max(tk, 1),), -1, dtype=torch.int32, device=dev)
     x_perm = (torch.empty((max(tk, 1), cfg.D), dtype=act_torch_dtype(cfg), device=dev)
               if copy_rows else None)
@@ -208,7 +209,8 @@ def dispatch(cfg: Cfg, topk_idx, x, ws=None, stream=None, copy_rows=True):
     _check(lib().moe_dispatch(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts), _p(offsets),
                               _p(slot_pos), _p(perm), _p(x_perm), _p(ws), ws.numel(),
                               _stream(stream)))
-    return dict(counts=counts, offsets=offsets, slot_pos=slot_pos, perm=perm, x_perm=x_perm)
+    return dict(counts=counts, offsets=offsets, slot_pos=slot_pos[:cfg.T], perm=perm,
+                x_perm=x_perm)
 
 
 def dispatch_noalloc(cfg: Cfg, topk_idx, x, counts, offsets, slot_pos, perm, x_perm,

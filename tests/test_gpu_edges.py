@@ -120,9 +120,25 @@ def test_zero_tokens():
     x = torch.empty((1, 128), dtype=torch.bfloat16, device=dev)
     W_r = torch.zeros((128, 8), dtype=torch.float32, device=dev)
     w = moe.Weights(*(torch.empty(16, dtype=torch.bfloat16, device=dev) for _ in range(3)))
-    y = moe.forward(cfg, x, W_r, None, w)
+    counts = torch.full((8,), -7, dtype=torch.int32, device=dev)
+    offsets = torch.full((9,), -7, dtype=torch.int32, device=dev)
+    y = moe.forward(cfg, x, W_r, None, w, counts=counts, offsets=offsets)
     torch.cuda.synchronize()
     assert y.shape[0] == 1
+    # the empty layer's counts and offsets are zero, from moe_forward and
+    # from both dispatch entry points
+    assert (counts == 0).all() and (offsets == 0).all()
+    idx = torch.empty((1, cfg.top_k), dtype=torch.int32, device=dev)
+    d = moe.dispatch(cfg, idx, x)
+    torch.cuda.synchronize()
+    assert (d["counts"] == 0).all() and (d["offsets"] == 0).all()
+    counts.fill_(-7)
+    offsets.fill_(-7)
+    sp = torch.empty((1, cfg.top_k), dtype=torch.int32, device=dev)
+    perm = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.dispatch_noalloc(cfg, idx, x, counts, offsets, sp, perm, None)
+    torch.cuda.synchronize()
+    assert (counts == 0).all() and (offsets == 0).all()
 
 
 @pytest.mark.parametrize("wdt", [syn.BF16, syn.MXFP4], ids=["bf16", "mxfp4"])
