@@ -9,6 +9,13 @@
 #include "../../include/moe.h"
 #include "launch.h"
 
+namespace moe {
+// dispatch.hip: T = 0, counts [E] and offsets [E + 1] (either may be null)
+// set to zero
+hipError_t launch_dispatch_empty(const moe_cfg& c, int32_t* counts, int32_t* offsets,
+                                 hipStream_t s);
+}  // namespace moe
+
 namespace {
 
 thread_local int g_last_hip_error = 0;

@@ -114,10 +114,7 @@ hipError_t launch_quant_mxfp8(const void* x, long long rows, int K, uint8_t* cod
                               bool grouped, hipStream_t s);
 hipError_t launch_gemm_a8(const GemmProblem& p, bool swiglu, hipStream_t s);
 
-// fp32 activations and weights: straightforward VALU kernels.
-// T = 0: counts [E] and offsets [E + 1] (either may be null) set to zero.
-hipError_t launch_dispatch_empty(const moe_cfg& c, int32_t* counts, int32_t* offsets,
-                                 hipStream_t s);
+// fp32 activations and weights: the grouped GEMM on the fp32 MFMA.
 hipError_t launch_ffn_f32_gate_up(const moe_cfg& c, const float* x_perm, const int32_t* offsets,
                                   const float* Wg, const float* Wu, float* H, hipStream_t s);
 hipError_t launch_ffn_f32_down(const moe_cfg& c, const float* H, const int32_t* offsets,
