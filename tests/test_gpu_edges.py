@@ -105,6 +105,15 @@ def test_sigmoid_renorm_fp32():
     _run(cfg)
 
 
+def test_fp32_many_experts():
+    """fp32 MFMA GEMM whose workgroups find their expert among more than 64
+    (the segment-length scan runs over two 64-expert chunks), with segments
+    of a few rows each."""
+    cfg = syn.Config("fp32e100", T=300, D=64, E=100, k=3, F=72, act=syn.F32, wdt=syn.F32,
+                     gating=syn.GATE_SOFTMAX, renorm=1, bias="normal", bias_sigma=0.5)
+    _run(cfg)
+
+
 def test_fp32_clamp_multi_tile():
     """fp32 MFMA GEMM with an active clamp on gate and up (|pre-activation|
     has sigma about 0.02 sqrt(D) = 0.3, so a bound of 0.2 clamps a large share
