@@ -54,8 +54,6 @@ int check_cfg(const moe_cfg* c) {
   if (bf) {
     if (c->D % 32 || c->F % 32) return MOE_ERR_UNSUPPORTED;  // GEMM K steps of 32
     if (is_a8(*c) && (c->D % 64 || c->F % 64)) return MOE_ERR_UNSUPPORTED;  // and of 64
-  } else {
-    if (c->D > 16384 || c->F > 16384) return MOE_ERR_UNSUPPORTED;
   }
   if (c->shared_F > 0) {
     if (c->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;

@@ -114,6 +114,15 @@ def test_fp32_many_experts():
     _run(cfg)
 
 
+def test_fp32_wide_rows():
+    """fp32 layer with D above 16384 (no size limit on the fp32 path: the
+    GEMM streams K through LDS, the router falls back to its general
+    few-expert kernel beyond 4096)."""
+    cfg = syn.Config("fp32wide", T=40, D=16400, E=4, k=2, F=64, act=syn.F32, wdt=syn.F32,
+                     gating=syn.GATE_SOFTMAX, renorm=1)
+    _run(cfg)
+
+
 def test_fp32_clamp_multi_tile():
     """fp32 MFMA GEMM with an active clamp on gate and up (|pre-activation|
     has sigma about 0.02 sqrt(D) = 0.3, so a bound of 0.2 clamps a large share
