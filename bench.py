@@ -615,7 +615,11 @@ def main():
     gemm_tf = tfs(work["gate_up_flop"] + work["down_flop"], stage_ms["gate_up"] + stage_ms["down"])
     stage_report = {
         "route": {"ms": stage_ms["route"], "GB/s": gbs(work["route_bytes"], stage_ms["route"])},
-        "dispatch": {"ms": stage_ms["dispatch"], "GB/s": gbs(work["dispatch_bytes"], stage_ms["dispatch"])},
+        "dispatch": {"ms": stage_ms["dispatch"], "GB/s": gbs(work["dispatch_bytes"], stage_ms["dispatch"]),
+                     "bytes": work["dispatch_bytes"],
+                     "note": ("index work only (counts, offsets, ranks): the gate/up GEMM gathers "
+                              "the rows from x, so no row is copied" if gathered else
+                              "indices and the row copy into x_perm")},
         "gate_up": {"ms": stage_ms["gate_up"], "TFLOP/s": gu_tf},
         "down": {"ms": stage_ms["down"], "TFLOP/s": dn_tf},
         "combine": {"ms": stage_ms["combine"], "GB/s": gbs(work["combine_bytes"], stage_ms["combine"])},
@@ -626,7 +630,8 @@ def main():
     flushed = {n: {"ms": fl_ms[n], "GB/s": gbs(work[f"{n}_bytes"], fl_ms[n])}
                for n in ("route", "dispatch", "combine")}
     for n in order:
-        log(f"[bench] {n:9s} " + "  ".join(f"{kk} {vv:9.3f}" for kk, vv in stage_report[n].items()))
+        log(f"[bench] {n:9s} " + "  ".join(f"{kk} {vv:9.3f}" for kk, vv in stage_report[n].items()
+                                           if kk in ("ms", "GB/s", "TFLOP/s")))
     log(f"[bench] grouped GEMM {gemm_tf:.1f} TFLOP/s = "
         f"{100 * gemm_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
     log("[bench] MALL flushed: " + "  ".join(f"{n} {v['ms']:.3f} ms {v['GB/s']:.0f} GB/s"
