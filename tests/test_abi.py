@@ -104,3 +104,41 @@ def test_workspace_sizes_cover_the_buffers():
     assert moe.workspace_size(f32, moe.WS_FORWARD) >= tk * D * 4 + tk * F * 4 + tk * D * 4
     assert moe.workspace_size(c, moe.WS_DISPATCH) >= 8 * 16 * 4
     assert moe.workspace_size(c, moe.WS_EXPERT_FFN) >= 4 * (1 + 2 * (tk // 128 + 8))
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "moe.h"
+/* a C caller of the whole layer: compiles against the header as C99 */
+int call_layer(const void* x, const float* W_r, const float* bias, const void* wg,
+               const void* wu, const void* wd, void* y, void* ws, void* stream) {
+  moe_cfg cfg = {.T = 4096, .D = 4096, .E = 8, .F = 14336, .top_k = 2,
+                 .gating = MOE_GATE_SOFTMAX, .renorm = 1, .capacity = 0, .clamp = 0.0f,
+                 .act_dtype = MOE_BF16, .w_dtype = MOE_BF16, .shared_F = 0};
+  moe_weights w = {.W_gate = wg, .W_up = wu, .W_down = wd};
+  size_t bytes = 0;
+  int st = moe_workspace_size(&cfg, MOE_WS_FORWARD, &bytes);
+  if (st != MOE_OK) return st;
+  st = moe_forward(&cfg, x, W_r, bias, &w, y, NULL, NULL, NULL, NULL, ws, bytes, stream);
+  if (st != MOE_OK) fprintf(stderr, "%s\n", moe_status_string(st));
+  return st;
+}
+"""
+
+
+def test_header_compiles_as_c99(tmp_path):
+    """include/moe.h is plain C: a C99 caller compiles against it with every
+    warning an error, and links against the library."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    lib_dir = os.path.dirname(moe.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                        str(tmp_path / "libcaller.so"), "-L", lib_dir, "-lmoe"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
