@@ -384,13 +384,13 @@ __device__ __forceinline__ void for_each_index(F&& f) {
 // candidate list. More units than threads: further passes over d.
 //
 // The time goes to the chains themselves (a variant without them runs in
-// 14-22 us of the 75-155), i.e. to the longest run of chain steps on one
-// SIMD: UT chains per lane, each a conversion and an FMA per term. The
-// small tiles (about 190 pairs on the 128-expert layer) run one chain per
-// unit (UT = 1) in three busy waves; the large ones (about 670 pairs on
-// the 384-expert layer) three per unit, with units dealt round-robin to
-// waves 0..3 (BAL) so that all four SIMDs carry about 56 lanes of 3 chains
-// rather than three SIMDs 64 lanes of 4 (136 against 155 us).
+// 14-22 us of the 75-155): UT chains per lane, each an unpack and an FMA
+// per term. A token keeps about 14 candidates of 128 or 384 experts, so a
+// 64 x 32 tile holds about 220 pairs and a 256 x 96 tile about 940. The
+// small tiles run one chain per unit (UT = 1); the large ones three, with
+// the units dealt round-robin to waves 0..3 and then 4..7 (BAL). Measured
+// against the other unit sizes, prefetch depths and dealings (4 chains,
+// 2 chains, consecutive units per wave): these were the fastest.
 template <int TB, int ERX, int UT, int PF, bool BAL>
 __global__ __launch_bounds__(512) void screen_exact_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wt, const float* __restrict__ bias,
