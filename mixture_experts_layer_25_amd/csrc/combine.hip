@@ -87,12 +87,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         acc[u][4] += b.x; acc[u][5] += b.y; acc[u][6] += b.z; acc[u][7] += b.w;
       }
       if (OUT_BF16) {
-        uint4 o;
-        o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-        o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-        o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-        o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-        reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (size_t)t * D)[v] = o;
+        // y is written once and not read again here: non-temporal stores
+        // (384- and 128-expert layers 2-3 % faster, the 8-expert layer
+        // within 1.5 %, with the MALL flushed before each run)
+        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+        const u32x4v o = {pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
+                          pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7])};
+        __builtin_nontemporal_store(
+            o, reinterpret_cast<u32x4v*>(static_cast<uint16_t*>(y) + (size_t)t * D) + v);
       } else {
         float4* dst = reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * D) + 2 * v;
         dst[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
